@@ -1,0 +1,11 @@
+"""Chunkwise gated delta rule forward (Gated DeltaNet / KDA) for MI355X.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
+declared in include/gdr.h (libgdr.so, built in-tree by ``build.py``); this
+package is the thin Python binding over it plus the seeded input generator.
+"""
+from .binding import (GDR_BF16, GDR_F32, EXPORTED, GdrError, GdrProblem, LIB_PATH,  # noqa: F401
+                      check, gdr_chunk_fwd, gdr_chunk_prep, gdr_chunk_scan, load, problem,
+                      status_string, workspace_size)
+
+__version__ = "0.1.0"

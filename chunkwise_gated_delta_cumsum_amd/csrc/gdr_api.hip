@@ -1,0 +1,314 @@
+// C ABI of the chunkwise gated delta rule forward pass (declared in gdr.h).
+//
+// Host side only: argument validation (no HIP call before it passes), the
+// workspace layout, the gfx950 check, and the launches of the two kernels
+// on the caller's stream.  The library allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gdr.h"
+#include "gdr_device.hpp"
+#include "gdr_prep.hpp"
+#include "gdr_scan.hpp"
+
+using namespace gdr;
+
+namespace {
+
+constexpr int kScanBV = 32;  // value columns per scan workgroup (16 per wave)
+
+struct Prob {
+  int B, T, H, HV, K, V, N;
+  bool perch, f32;
+  float scale;
+  size_t es;  // bytes per q/k/v element and per workspace fragment element
+};
+
+gdr_status validate(const gdr_problem* p, Prob* out) {
+  if (!p) return GDR_ERR_NULL;
+  if (p->B < 1 || p->T < 1 || p->H < 1 || p->HV < 1 || p->K < 1 || p->V < 1 ||
+      p->HV % p->H != 0)
+    return GDR_ERR_SHAPE;
+  if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
+  if (p->g_per_channel != 0 && p->g_per_channel != 1) return GDR_ERR_ARG;
+  if (!std::isfinite(p->scale)) return GDR_ERR_ARG;
+  if (p->chunk != kChunk) return GDR_ERR_UNSUPPORTED;
+  if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
+  Prob r;
+  r.B = p->B; r.T = p->T; r.H = p->H; r.HV = p->HV; r.K = p->K; r.V = p->V;
+  r.N = (p->T + kChunk - 1) / kChunk;
+  r.perch = p->g_per_channel == 1;
+  r.f32 = p->qkv_dtype == GDR_F32;
+  r.scale = p->scale;
+  r.es = r.f32 ? 4 : 2;
+  // grid sizes must fit a 32-bit launch dimension
+  if ((uint64_t)r.B * r.HV * r.N > 0x7fffffffull) return GDR_ERR_SHAPE;
+  if (out) *out = r;
+  return GDR_OK;
+}
+
+size_t nchunks(const Prob& r) { return (size_t)r.B * r.HV * r.N; }
+
+WsLayout layout(const Prob& r) { return ws_layout(nchunks(r), r.K, r.perch, r.es); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+struct Spans {
+  Span q, k, v, g, beta, s0, o, sT, ws;
+};
+
+Spans spans(const Prob& r, const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* s0, const float* o, const float* sT,
+            const void* ws, size_t ws_bytes) {
+  const size_t tok = (size_t)r.B * r.T;
+  Spans s;
+  s.q = {q, tok * r.H * r.K * r.es};
+  s.k = {k, tok * r.H * r.K * r.es};
+  s.v = {v, tok * r.HV * r.V * r.es};
+  s.g = {g, tok * r.HV * (r.perch ? r.K : 1) * sizeof(float)};
+  s.beta = {beta, tok * r.HV * sizeof(float)};
+  s.s0 = {s0, (size_t)r.B * r.HV * r.K * r.V * sizeof(float)};
+  s.o = {o, tok * r.HV * r.V * sizeof(float)};
+  s.sT = {sT, (size_t)r.B * r.HV * r.K * r.V * sizeof(float)};
+  s.ws = {ws, ws_bytes};
+  return s;
+}
+
+// An output span must not overlap any input span.
+bool out_overlaps(Span out, std::initializer_list<Span> ins) {
+  for (const Span& in : ins)
+    if (overlap(out, in)) return true;
+  return false;
+}
+
+gdr_status check_device() {
+  static std::atomic<int> verdict[64];  // 0 unknown, 1 gfx950, 2 other (per device ordinal)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    const int v = verdict[dev].load(std::memory_order_relaxed);
+    if (v == 1) return GDR_OK;
+    if (v == 2) return GDR_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GDR_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) verdict[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? GDR_OK : GDR_ERR_DEVICE;
+}
+
+template <class Kern, class Args>
+gdr_status launch(Kern kern, unsigned grid, unsigned block, Args& args, hipStream_t s) {
+  void* kargs[] = {&args};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid),
+                                       dim3(block), kargs, 0, s);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+template <int K, bool PERCH, class P>
+gdr_status launch_prep_k(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
+  const unsigned grid = (unsigned)nchunks(r);
+  if (dump) return launch(chunk_prep_kernel<K, PERCH, P, true>, grid, 256, a, s);
+  return launch(chunk_prep_kernel<K, PERCH, P, false>, grid, 256, a, s);
+}
+
+template <bool PERCH, class P>
+gdr_status launch_prep_p(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
+  return r.K == 64 ? launch_prep_k<64, PERCH, P>(r, a, dump, s)
+                   : launch_prep_k<128, PERCH, P>(r, a, dump, s);
+}
+
+gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
+  if (r.f32)
+    return r.perch ? launch_prep_p<true, PolicyF32>(r, a, dump, s)
+                   : launch_prep_p<false, PolicyF32>(r, a, dump, s);
+  return r.perch ? launch_prep_p<true, PolicyF16>(r, a, dump, s)
+                 : launch_prep_p<false, PolicyF16>(r, a, dump, s);
+}
+
+template <int K, int V, bool PERCH, class P>
+gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
+  constexpr int BV = kScanBV;
+  const unsigned grid = (unsigned)((size_t)r.B * r.HV * (V / BV));
+  return launch(chunk_scan_kernel<K, V, BV, PERCH, P>, grid, BV / 16 * 64, a, s);
+}
+
+template <bool PERCH, class P>
+gdr_status launch_scan_p(const Prob& r, ScanArgs& a, hipStream_t s) {
+  if (r.K == 64)
+    return r.V == 64 ? launch_scan_kv<64, 64, PERCH, P>(r, a, s)
+                     : launch_scan_kv<64, 128, PERCH, P>(r, a, s);
+  return r.V == 64 ? launch_scan_kv<128, 64, PERCH, P>(r, a, s)
+                   : launch_scan_kv<128, 128, PERCH, P>(r, a, s);
+}
+
+gdr_status launch_scan(const Prob& r, ScanArgs& a, hipStream_t s) {
+  if (r.f32)
+    return r.perch ? launch_scan_p<true, PolicyF32>(r, a, s)
+                   : launch_scan_p<false, PolicyF32>(r, a, s);
+  return r.perch ? launch_scan_p<true, PolicyF16>(r, a, s)
+                 : launch_scan_p<false, PolicyF16>(r, a, s);
+}
+
+PrepArgs prep_args(const Prob& r, const void* q, const void* k, const float* g,
+                   const float* beta, void* ws) {
+  const WsLayout L = layout(r);
+  char* base = static_cast<char*>(ws);
+  PrepArgs a;
+  a.q = q; a.k = k; a.g = g; a.beta = beta;
+  a.B = r.B; a.T = r.T; a.H = r.H; a.HV = r.HV; a.N = r.N;
+  a.scale = r.scale;
+  a.wt = base + L.wt; a.ah = base + L.ah; a.rs = reinterpret_cast<float*>(base + L.rs);
+  a.qh = base + L.qh; a.kh = base + L.kh;
+  a.d_gamma = a.d_akk = a.d_aqk = a.d_minv = nullptr;
+  return a;
+}
+
+ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
+                   const float* s0, float* o, float* sT, const void* ws) {
+  const WsLayout L = layout(r);
+  const char* base = static_cast<const char*>(ws);
+  ScanArgs a;
+  a.q = q; a.k = k; a.v = v; a.s0 = s0; a.o = o; a.sT = sT;
+  a.wt = base + L.wt; a.ah = base + L.ah; a.rs = reinterpret_cast<const float*>(base + L.rs);
+  a.qh = base + L.qh; a.kh = base + L.kh;
+  a.B = r.B; a.T = r.T; a.H = r.H; a.HV = r.HV; a.N = r.N;
+  a.scale = r.scale;
+  return a;
+}
+
+gdr_status check_ws(const Prob& r, const void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < layout(r).total) return GDR_ERR_WORKSPACE;
+  if (!aligned16(ws)) return GDR_ERR_ALIGN;
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
+  Prob r;
+  if (validate(p, &r) != GDR_OK) return 0;
+  return layout(r).total;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         float* o, float* final_state, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Prob r;
+  gdr_status st = validate(p, &r);
+  if (st != GDR_OK) return st;
+  if (!q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
+                          (const void*)beta, (const void*)initial_state, (const void*)o,
+                          (const void*)final_state})
+    if (ptr && !aligned16(ptr)) return GDR_ERR_ALIGN;
+  if ((st = check_ws(r, workspace, workspace_bytes)) != GDR_OK) return st;
+  const Spans s = spans(r, q, k, v, g, beta, initial_state, o, final_state, workspace,
+                        workspace_bytes);
+  if (out_overlaps(s.o, {s.q, s.k, s.v, s.g, s.beta, s.s0, s.sT, s.ws})) return GDR_ERR_ALIAS;
+  if (out_overlaps(s.ws, {s.q, s.k, s.v, s.g, s.beta, s.s0, s.sT})) return GDR_ERR_ALIAS;
+  if (out_overlaps(s.sT, {s.q, s.k, s.v, s.g, s.beta})) return GDR_ERR_ALIAS;
+  if (initial_state && final_state && initial_state != final_state && overlap(s.sT, s.s0))
+    return GDR_ERR_ALIAS;
+  if ((st = check_device()) != GDR_OK) return st;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  PrepArgs pa = prep_args(r, q, k, g, beta, workspace);
+  if ((st = launch_prep(r, pa, false, hs)) != GDR_OK) return st;
+  ScanArgs sa = scan_args(r, q, k, v, initial_state, o, final_state, workspace);
+  return launch_scan(r, sa, hs);
+}
+
+gdr_status gdr_chunk_prep(const gdr_problem* p, const void* q, const void* k, const float* g,
+                          const float* beta, void* workspace, size_t workspace_bytes,
+                          float* gamma, float* a_kk, float* a_qk, float* m_inv, void* stream) {
+  Prob r;
+  gdr_status st = validate(p, &r);
+  if (st != GDR_OK) return st;
+  if (!q || !k || !g || !beta) return GDR_ERR_NULL;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)g, (const void*)beta,
+                          (const void*)gamma, (const void*)a_kk, (const void*)a_qk,
+                          (const void*)m_inv})
+    if (ptr && !aligned16(ptr)) return GDR_ERR_ALIGN;
+  if ((st = check_ws(r, workspace, workspace_bytes)) != GDR_OK) return st;
+  const Spans s = spans(r, q, k, nullptr, g, beta, nullptr, nullptr, nullptr, workspace,
+                        workspace_bytes);
+  if (out_overlaps(s.ws, {s.q, s.k, s.g, s.beta})) return GDR_ERR_ALIAS;
+  const size_t nc = nchunks(r);
+  const Span dg = {gamma, nc * kChunk * (r.perch ? r.K : 1) * sizeof(float)};
+  const Span dm = {a_kk, nc * kChunk * kChunk * sizeof(float)};
+  const Span da = {a_qk, nc * kChunk * kChunk * sizeof(float)};
+  const Span di = {m_inv, nc * kChunk * kChunk * sizeof(float)};
+  for (const Span& out : {dg, dm, da, di})
+    if (out_overlaps(out, {s.q, s.k, s.g, s.beta, s.ws})) return GDR_ERR_ALIAS;
+  if (overlap(dg, dm) || overlap(dg, da) || overlap(dg, di) || overlap(dm, da) ||
+      overlap(dm, di) || overlap(da, di))
+    return GDR_ERR_ALIAS;
+  if ((st = check_device()) != GDR_OK) return st;
+
+  PrepArgs pa = prep_args(r, q, k, g, beta, workspace);
+  pa.d_gamma = gamma; pa.d_akk = a_kk; pa.d_aqk = a_qk; pa.d_minv = m_inv;
+  const bool dump = gamma || a_kk || a_qk || m_inv;
+  return launch_prep(r, pa, dump, static_cast<hipStream_t>(stream));
+}
+
+gdr_status gdr_chunk_scan(const gdr_problem* p, const void* q, const void* k, const void* v,
+                          const float* initial_state, float* o, float* final_state,
+                          const void* workspace, size_t workspace_bytes, void* stream) {
+  Prob r;
+  gdr_status st = validate(p, &r);
+  if (st != GDR_OK) return st;
+  if (!q || !k || !v || !o) return GDR_ERR_NULL;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v,
+                          (const void*)initial_state, (const void*)o, (const void*)final_state})
+    if (ptr && !aligned16(ptr)) return GDR_ERR_ALIGN;
+  if ((st = check_ws(r, workspace, workspace_bytes)) != GDR_OK) return st;
+  const Spans s = spans(r, q, k, v, nullptr, nullptr, initial_state, o, final_state,
+                        workspace, workspace_bytes);
+  if (out_overlaps(s.o, {s.q, s.k, s.v, s.s0, s.sT, s.ws})) return GDR_ERR_ALIAS;
+  if (out_overlaps(s.sT, {s.q, s.k, s.v, s.ws})) return GDR_ERR_ALIAS;
+  if (initial_state && final_state && initial_state != final_state && overlap(s.sT, s.s0))
+    return GDR_ERR_ALIAS;
+  if ((st = check_device()) != GDR_OK) return st;
+  ScanArgs sa = scan_args(r, q, k, v, initial_state, o, final_state, workspace);
+  return launch_scan(r, sa, static_cast<hipStream_t>(stream));
+}
+
+const char* gdr_status_string(int status) {
+  switch (status) {
+    case GDR_OK: return "GDR_OK: success";
+    case GDR_ERR_NULL: return "GDR_ERR_NULL: a required pointer is NULL";
+    case GDR_ERR_SHAPE: return "GDR_ERR_SHAPE: B, T, H, HV, K, V must be >= 1 and HV % H == 0";
+    case GDR_ERR_DTYPE: return "GDR_ERR_DTYPE: qkv_dtype must be GDR_F32 or GDR_BF16";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: built for chunk 64 and K, V in {64, 128}";
+    case GDR_ERR_ALIGN: return "GDR_ERR_ALIGN: tensors and workspace must be 16-byte aligned";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace NULL or smaller than gdr_chunk_fwd_workspace_size";
+    case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE: the current HIP device is not gfx950";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP query or kernel launch failed";
+    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite and g_per_channel 0 or 1";
+    case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: an output overlaps an input or another output";
+    default: return "GDR_ERR_UNKNOWN: unknown status value";
+  }
+}
+
+int gdr_version(void) { return 100; }
+
+}  // extern "C"

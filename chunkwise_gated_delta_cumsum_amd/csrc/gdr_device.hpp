@@ -1,0 +1,212 @@
+// Device-side building blocks shared by the gfx950 kernels.
+//
+// MFMA fragment convention used everywhere in this library (wave64):
+//   lane l, r = l % 16, grp = l / 16.
+//   * A operand of a 16 x 32 tile: lane holds row r, 8 values at logical
+//     k = kslot(grp, i), i = 0..7.
+//   * B operand of a 32 x 16 tile: lane holds column r at the same k slots.
+//   * C/D accumulator of a 16 x 16 tile: lane holds column r, rows 4*grp + j.
+// kslot(grp, i) = 4*grp + (i & 3) + 16*(i >> 2) is chosen so that two
+// vertically stacked accumulator tiles (rows 0-15 and 16-31) ARE a B operand
+// with k = row, and the accumulator of X is the A operand of X^T.  Products
+// therefore chain through registers without a transpose.  Both operands of
+// every product use the same k slots, so the hardware's own k order inside
+// an instruction does not matter.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kChunk = 64;
+
+__device__ __forceinline__ int kslot(int grp, int i) {
+  return 4 * grp + (i & 3) + 16 * (i >> 2);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- products -------------------------------------------------------------
+// 16x16 tile += (16 x 32) * (32 x 16)
+__device__ __forceinline__ f32x4 mma32(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+// 16x16 tile += (16 x 16) * (16 x 16) in fp32; lane holds k = 4*grp + i.
+__device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+// ---- precision policies ---------------------------------------------------
+// F16: bf16 inputs, fp16 MFMA operands, fp16 workspace fragments.
+// F32: fp32 inputs, fp32 MFMA, fp32 workspace fragments.
+struct PolicyF16 {
+  using in_t = uint16_t;   // bf16 bits
+  using frag_t = half8;
+  using ws_t = _Float16;
+  static constexpr bool kF32 = false;
+  __device__ static __forceinline__ float in_to_f32(in_t x) { return bf16_to_f32(x); }
+  __device__ static __forceinline__ frag_t make(const float* v) {
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (_Float16)v[i];
+    return f;
+  }
+  __device__ static __forceinline__ frag_t make2(f32x4 lo, f32x4 hi) {
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = (_Float16)lo[i]; f[4 + i] = (_Float16)hi[i]; }
+    return f;
+  }
+};
+
+struct PolicyF32 {
+  using in_t = float;
+  using frag_t = f32x8;
+  using ws_t = float;
+  static constexpr bool kF32 = true;
+  __device__ static __forceinline__ float in_to_f32(in_t x) { return x; }
+  __device__ static __forceinline__ frag_t make(const float* v) {
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = v[i];
+    return f;
+  }
+  __device__ static __forceinline__ frag_t make2(f32x4 lo, f32x4 hi) {
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+    return f;
+  }
+};
+
+// ---- fragment loads -------------------------------------------------------
+// A/B fragment of a row-contiguous source (row pointer already offset to the
+// first k of the 32-block): elements row[kslot(grp, i)].
+template <class P>
+__device__ __forceinline__ typename P::frag_t frag_row_f32(const float* row, int grp) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 + 4 * grp);
+  return P::make2(lo, hi);
+}
+
+// Same, from the input element type (bf16 bits or fp32), converted to the
+// policy's fragment type.
+__device__ __forceinline__ half8 frag_row_in(const uint16_t* row, int grp, PolicyF16) {
+  u16x4 lo = *reinterpret_cast<const u16x4*>(row + 4 * grp);
+  u16x4 hi = *reinterpret_cast<const u16x4*>(row + 16 + 4 * grp);
+  half8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = (_Float16)bf16_to_f32(lo[i]);
+    f[4 + i] = (_Float16)bf16_to_f32(hi[i]);
+  }
+  return f;
+}
+__device__ __forceinline__ f32x8 frag_row_in(const float* row, int grp, PolicyF32) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 + 4 * grp);
+  f32x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+  return f;
+}
+
+// Raw bf16 fragment (no conversion) for exact bf16 x bf16 Gram products.
+__device__ __forceinline__ bf16x8 frag_row_bf16(const uint16_t* row, int grp) {
+  u16x4 lo = *reinterpret_cast<const u16x4*>(row + 4 * grp);
+  u16x4 hi = *reinterpret_cast<const u16x4*>(row + 16 + 4 * grp);
+  u16x8 u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { u[i] = lo[i]; u[4 + i] = hi[i]; }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Workspace fragment: 8 consecutive ws_t per lane.
+__device__ __forceinline__ half8 frag_ws(const _Float16* p) {
+  return *reinterpret_cast<const half8*>(p);
+}
+__device__ __forceinline__ f32x8 frag_ws(const float* p) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
+  return f;
+}
+__device__ __forceinline__ void store_ws(_Float16* p, f32x4 lo, f32x4 hi) {
+  half8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[i] = (_Float16)lo[i]; f[4 + i] = (_Float16)hi[i]; }
+  *reinterpret_cast<half8*>(p) = f;
+}
+__device__ __forceinline__ void store_ws(float* p, f32x4 lo, f32x4 hi) {
+  *reinterpret_cast<f32x4*>(p) = lo;
+  *reinterpret_cast<f32x4*>(p + 4) = hi;
+}
+__device__ __forceinline__ void store_ws8(_Float16* p, const float* v) {
+  half8 f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (_Float16)v[i];
+  *reinterpret_cast<half8*>(p) = f;
+}
+__device__ __forceinline__ void store_ws8(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// ---- workspace layout -----------------------------------------------------
+// Per chunk (one value head, C = 64 rows), in fragment order so every lane
+// reads or writes 8 consecutive elements:
+//   wt : W^ = M^-T diag(beta exp(gamma_last - gamma)) k   as the A operand of
+//        W^T (rows d, k = c): [K/16 row tiles][2 k-blocks][64 lanes][8]
+//   ah : A^ = A_qk M^-1 as an A operand (rows i, k = c): [4][2][64][8]
+//   rs : 256 fp32: [0..63] exp(gamma_c) (one decay per row; 1 per channel),
+//        [64..64+K) exp(gamma_last) per key channel
+//   qh, kh (per-channel decay only): q exp(gamma) scale and k exp(gamma) as A
+//        operands (rows c, k = d): [4][K/32][64][8]
+struct WsLayout {
+  size_t wt, ah, rs, qh, kh, total;
+};
+
+__host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline WsLayout ws_layout(size_t nchunks, int K, bool per_channel,
+                                              size_t elem) {
+  WsLayout L;
+  size_t off = 0;
+  L.wt = off; off = ws_align(off + nchunks * (size_t)K * kChunk * elem);
+  L.ah = off; off = ws_align(off + nchunks * (size_t)kChunk * kChunk * elem);
+  L.rs = off; off = ws_align(off + nchunks * 256 * sizeof(float));
+  L.qh = L.kh = off;
+  if (per_channel) {
+    L.qh = off; off = ws_align(off + nchunks * (size_t)kChunk * K * elem);
+    L.kh = off; off = ws_align(off + nchunks * (size_t)kChunk * K * elem);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace gdr

@@ -1,0 +1,138 @@
+/*
+ * gdr.h -- C ABI of the chunkwise gated delta rule forward pass for MI355X
+ * (gfx950).  Plain C: no C++ or torch types cross this boundary.
+ *
+ * The operation (sec-03 notes "Chunkwise": in-chunk cumsum and triangular
+ * solve, code comparison, inter-chunk recurrence; "Chunkwise parallel
+ * algorithms" page, sections 2.1-2.4) maps, for every batch b and value head
+ * hv with q/k head h = hv / (HV/H),
+ *
+ *     S <- diag(exp(g_t)) S ;  S <- S + beta_t k_t (v_t - S^T k_t)^T ;
+ *     o_t = scale * S^T q_t                            (t = 0 .. T-1)
+ *
+ * and computes it chunkwise with chunk length C: in-chunk cumsum gamma of g,
+ * the decayed dot matrices A_kk and A_qk, the UT transform (the inverse of
+ * M = I + strictly_lower(A_kk diag(beta))), and the serial inter-chunk
+ * recurrence of the K x V state.  The result equals that recurrence up to
+ * floating-point rounding.
+ *
+ * Tensor layouts (row-major, contiguous, device memory):
+ *   q, k           [B, T, H, K]    qkv_dtype (GDR_F32 or GDR_BF16)
+ *   v              [B, T, HV, V]   qkv_dtype
+ *   g              [B, T, HV] fp32 (one log-decay per value head), or
+ *                  [B, T, HV, K] fp32 when g_per_channel = 1 (KDA form)
+ *   beta           [B, T, HV]      fp32
+ *   initial_state  [B, HV, K, V]   fp32, or NULL for a zero state
+ *   o              [B, T, HV, V]   fp32 (output)
+ *   final_state    [B, HV, K, V]   fp32 (output), or NULL to skip
+ *
+ * Ownership: the caller allocates and owns every buffer, the workspace
+ * included.  The library never allocates or frees device memory and keeps
+ * no mutable global state; calls on different streams are independent.
+ *
+ * Streams: work is enqueued asynchronously on `stream` (a hipStream_t; NULL
+ * is the null stream).  No call synchronises.  A fault inside a kernel shows
+ * up at the caller's next synchronisation.
+ *
+ * Errors: arguments are validated before any HIP call.  On an error nothing
+ * is launched and a status other than GDR_OK is returned; no exception
+ * crosses the ABI.  gdr_status_string() names every status.
+ *
+ * Numerics: with GDR_BF16 inputs the matrix products run on MFMA with fp16
+ * operands and fp32 accumulation; the state, gamma, exponentials and o are
+ * fp32.  bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
+ * inputs every product runs in fp32.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_ERR_NULL = 1,        /* a required pointer (problem, q, k, v, g, beta, o) is NULL */
+  GDR_ERR_SHAPE = 2,       /* B, T, H, HV, K or V < 1, or HV % H != 0 */
+  GDR_ERR_DTYPE = 3,       /* qkv_dtype is not a gdr_dtype value */
+  GDR_ERR_UNSUPPORTED = 4, /* valid but not built: chunk != 64, K or V not 64 or 128 */
+  GDR_ERR_ALIGN = 5,       /* a tensor or workspace pointer is not 16-byte aligned */
+  GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query */
+  GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
+  GDR_ERR_HIP = 8,         /* a HIP query or kernel launch failed */
+  GDR_ERR_ARG = 9,         /* scale not finite, or g_per_channel not 0/1 */
+  GDR_ERR_ALIAS = 10       /* an output overlaps an input or the other output
+                              (final_state == initial_state exactly is allowed) */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef struct gdr_problem {
+  int32_t B, T, H, HV, K, V; /* batch, tokens, q/k heads, value heads, key dim, value dim */
+  int32_t chunk;             /* chunk length C; 64 is built */
+  int32_t g_per_channel;     /* 0: g[B,T,HV]; 1: g[B,T,HV,K] */
+  float scale;               /* query scale; callers usually pass 1/sqrt(K) */
+  int32_t qkv_dtype;         /* gdr_dtype of q, k and v */
+} gdr_problem;
+
+/* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when
+ * `p` is NULL or fails validation.  The size grows linearly with
+ * B * HV * ceil(T / chunk). */
+size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p);
+
+/* The whole forward pass: chunk preparation (cumsum, decayed dots, masks and
+ * the UT inverse, all per chunk in parallel) followed by the state scan over
+ * chunks.  Writes o for t < T and, when final_state is not NULL, the state
+ * after token T-1.  T need not be a multiple of the chunk length: rows past T
+ * are treated as padding with g = 0 and beta = 0, which leaves the state
+ * unchanged. */
+gdr_status gdr_chunk_fwd(const gdr_problem* p,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* initial_state,
+                         float* o, float* final_state,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Stage 1 alone (sec-03 notes: in-chunk cumsum, decayed dot, triangular
+ * system; UT transform): fills the workspace for gdr_chunk_scan.  With the
+ * inspection pointers non-NULL it also writes, in fp32 on the padded chunk
+ * grid with N = ceil(T / chunk):
+ *   gamma  [B, HV, N, C] (or [B, HV, N, C, K] per channel): in-chunk cumsum of g
+ *   a_kk   [B, HV, N, C, C]: strictly lower A_kk with beta on columns (= M - I)
+ *   a_qk   [B, HV, N, C, C]: lower A_qk (diagonal kept) with beta and scale
+ *   m_inv  [B, HV, N, C, C]: M^-1, the UT transform's inverse
+ * Any of them may be NULL. */
+gdr_status gdr_chunk_prep(const gdr_problem* p,
+                          const void* q, const void* k,
+                          const float* g, const float* beta,
+                          void* workspace, size_t workspace_bytes,
+                          float* gamma, float* a_kk, float* a_qk, float* m_inv,
+                          void* stream);
+
+/* Stage 2 alone (sec-03 notes, inter-chunk recurrence): the serial scan over
+ * chunks using a workspace filled by gdr_chunk_prep for the same problem and
+ * the same q, k, g, beta.  r = U - W S, o = (q exp(gamma)) S + A_qk r,
+ * S <- diag(exp(gamma_last)) S + (exp(gamma_last - gamma) k)^T (beta r),
+ * with W = M^-1 (exp(gamma) k) and U = M^-1 v folded into the workspace. */
+gdr_status gdr_chunk_scan(const gdr_problem* p,
+                          const void* q, const void* k, const void* v,
+                          const float* initial_state,
+                          float* o, float* final_state,
+                          const void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Static, never-NULL text for any status value (unknown values included). */
+const char* gdr_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

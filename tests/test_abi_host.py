@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function include/gdr.h declares, and
+reject bad arguments with the documented status before any HIP call.  All
+calls here fail validation, so they return before touching a device; the
+pointers are fake, 16-byte-aligned addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_gated_delta_cumsum_amd as gdr
+from chunkwise_gated_delta_cumsum_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from chunkwise_gated_delta_cumsum_amd import build
+        build.build()
+    return gdr.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_code_object(lib):
+    data = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS_NAMES.items():
+        assert gdr.status_string(code).startswith(name)
+    assert gdr.status_string(12345).startswith("GDR_ERR_UNKNOWN")
+    assert lib.gdr_version() >= 100
+
+
+A = 1 << 20   # fake device addresses, spaced far apart, 16-byte aligned
+
+
+def call_fwd(lib, prob, q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, s0=None,
+             o=6 * A, sT=7 * A, ws=8 * A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = gdr.workspace_size(prob) if gdr.workspace_size(prob) else 1 << 30
+    return lib.gdr_chunk_fwd(ctypes.byref(prob), q, k, v, g, beta, s0, o, sT, ws,
+                             ws_bytes, None)
+
+
+def base(**kw):
+    args = dict(B=1, T=100, H=2, HV=4, K=128, V=128)
+    args.update(kw)
+    return gdr.problem(**args)
+
+
+def test_workspace_size(lib):
+    p = base()
+    n = 1 * 4 * 2   # B * HV * ceil(100 / 64)
+    expect_min = n * (128 * 64 * 2 + 64 * 64 * 2 + 256 * 4)
+    assert gdr.workspace_size(p) >= expect_min
+    assert gdr.workspace_size(base(per_channel=True)) > gdr.workspace_size(p)
+    assert gdr.workspace_size(base(dtype="fp32")) > gdr.workspace_size(p)
+    assert gdr.workspace_size(base(HV=3)) == 0          # invalid -> 0
+    assert lib.gdr_chunk_fwd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), "GDR_ERR_SHAPE"),
+    (dict(T=0), "GDR_ERR_SHAPE"),
+    (dict(H=3, HV=4), "GDR_ERR_SHAPE"),
+    (dict(K=96), "GDR_ERR_UNSUPPORTED"),
+    (dict(V=256), "GDR_ERR_UNSUPPORTED"),
+    (dict(chunk=32), "GDR_ERR_UNSUPPORTED"),
+    (dict(scale=float("nan")), "GDR_ERR_ARG"),
+    (dict(scale=float("inf")), "GDR_ERR_ARG"),
+])
+def test_invalid_problem(lib, kw, status):
+    assert binding.STATUS_NAMES[call_fwd(lib, base(**kw))] == status
+
+
+def test_invalid_dtype_and_flag(lib):
+    p = base()
+    p.qkv_dtype = 7
+    assert binding.STATUS_NAMES[call_fwd(lib, p)] == "GDR_ERR_DTYPE"
+    p = base()
+    p.g_per_channel = 2
+    assert binding.STATUS_NAMES[call_fwd(lib, p)] == "GDR_ERR_ARG"
+
+
+def test_null_pointers(lib):
+    assert binding.STATUS_NAMES[lib.gdr_chunk_fwd(None, *([A] * 8), A, 1 << 30, None)] == "GDR_ERR_NULL"
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(beta=None), dict(o=None)):
+        assert binding.STATUS_NAMES[call_fwd(lib, base(), **kw)] == "GDR_ERR_NULL", kw
+
+
+def test_alignment(lib):
+    for kw in (dict(q=A + 8), dict(v=3 * A + 2), dict(o=6 * A + 4), dict(s0=9 * A + 8),
+               dict(sT=7 * A + 12), dict(ws=8 * A + 8)):
+        assert binding.STATUS_NAMES[call_fwd(lib, base(), **kw)] == "GDR_ERR_ALIGN", kw
+
+
+def test_workspace_checks(lib):
+    p = base()
+    need = gdr.workspace_size(p)
+    assert binding.STATUS_NAMES[call_fwd(lib, p, ws=None)] == "GDR_ERR_WORKSPACE"
+    assert binding.STATUS_NAMES[call_fwd(lib, p, ws_bytes=need - 1)] == "GDR_ERR_WORKSPACE"
+
+
+def test_aliasing(lib):
+    p = base()
+    assert binding.STATUS_NAMES[call_fwd(lib, p, o=A)] == "GDR_ERR_ALIAS"          # o == q
+    assert binding.STATUS_NAMES[call_fwd(lib, p, o=3 * A + 4096)] == "GDR_ERR_ALIAS"  # inside v
+    assert binding.STATUS_NAMES[call_fwd(lib, p, ws=5 * A)] == "GDR_ERR_ALIAS"     # ws == beta
+    assert binding.STATUS_NAMES[call_fwd(lib, p, sT=2 * A)] == "GDR_ERR_ALIAS"     # S == k
+    assert binding.STATUS_NAMES[call_fwd(lib, p, s0=9 * A, sT=9 * A + 64)] == "GDR_ERR_ALIAS"
+
+
+def test_stage_entry_points_validate(lib):
+    p = base()
+    ws = gdr.workspace_size(p)
+    st = lib.gdr_chunk_prep(ctypes.byref(p), None, 2 * A, 4 * A, 5 * A, 8 * A, ws,
+                            None, None, None, None, None)
+    assert binding.STATUS_NAMES[st] == "GDR_ERR_NULL"
+    st = lib.gdr_chunk_prep(ctypes.byref(p), A, 2 * A, 4 * A, 5 * A, 8 * A, ws,
+                            9 * A + 4, None, None, None, None)
+    assert binding.STATUS_NAMES[st] == "GDR_ERR_ALIGN"
+    st = lib.gdr_chunk_prep(ctypes.byref(p), A, 2 * A, 4 * A, 5 * A, 8 * A, ws,
+                            A, None, None, None, None)
+    assert binding.STATUS_NAMES[st] == "GDR_ERR_ALIAS"
+    st = lib.gdr_chunk_scan(ctypes.byref(p), A, 2 * A, 3 * A, None, 6 * A, 7 * A,
+                            8 * A, ws - 1, None)
+    assert binding.STATUS_NAMES[st] == "GDR_ERR_WORKSPACE"
+    st = lib.gdr_chunk_scan(ctypes.byref(p), A, 2 * A, 3 * A, None, 8 * A, 7 * A,
+                            8 * A, ws, None)
+    assert binding.STATUS_NAMES[st] == "GDR_ERR_ALIAS"
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load()
