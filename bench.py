@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise gated delta rule forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one forward pass over one batch of the workload: the chunk-prep
+kernel then the state-scan kernel (exactly the launch sequence of
+gdr_chunk_fwd, issued through the two stage entry points so that HIP events
+can bracket each kernel on the stream they run on).  Inputs are resident in
+HBM before the timed region; the step rotates through several copies of the
+inputs and outputs so that no step finds its data in the 256 MB last-level
+cache.  Prints one JSON line.
+
+Workload (default): B=1, T=4096, H=HV=12, K=V=128, chunk 64, scalar decay,
+bf16 q/k/v, fp32 g/beta/o/state: the 4096-token, 12-local-head shape whose
+intra-chunk matrix memory the scalar-g kernel page estimates.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+WORKLOAD_DEFAULT = "gdn_bf16_T4096_H12_D128"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def traffic_model(w):
+    """Algorithmic bytes per launch of each kernel and of the whole method.
+
+    Each tensor a kernel must read or write is counted once (q/k once per q/k
+    head); the workspace is what the prep kernel hands to the scan kernel.
+    """
+    C = w.chunk
+    N = -(-w.T // C)
+    nch = w.B * w.HV * N
+    tok = w.B * w.T
+    es = 4 if w.dtype == "fp32" else 2          # q/k/v element
+    wes = es                                    # workspace fragment element
+    qk = 2 * tok * w.H * w.K * es
+    v = tok * w.HV * w.V * es
+    g = tok * w.HV * (w.K if w.per_channel else 1) * 4
+    beta = tok * w.HV * 4
+    o = tok * w.HV * w.V * 4
+    state = w.B * w.HV * w.K * w.V * 4
+    s0 = state if w.s0_std > 0 else 0
+    ws = nch * (C * w.K * wes + C * C * wes + (64 + w.K) * 4)
+    qkh = 2 * nch * C * w.K * wes if w.per_channel else 0
+    prep = qk + g + beta + ws + qkh
+    scan = (qkh if w.per_channel else qk) + v + ws + s0 + o + state
+    compulsory = qk + v + g + beta + o + s0 + state
+    return dict(prep=prep, scan=scan, compulsory=compulsory)
+
+
+def algorithmic_flops(w):
+    """2 x MACs of the chunk algorithm (lower triangles only, no dense C x C work)."""
+    C, K, V, G = w.chunk, w.K, w.V, w.HV // w.H
+    mac = (((C - 1) / 2 * K + (C + 1) / 2 * K) / G + (C - 1) / 2 * (K + V) + 3 * K * V
+           + (C + 1) / 2 * V)
+    return 2.0 * mac * w.B * w.T * w.HV
+
+
+def cpu_baseline(inp, budget_s):
+    import oracle
+    w = inp.w
+    threads = min(os.cpu_count() or 1, w.B * w.HV)
+    # one pass over the whole workload if it fits the budget, else a token prefix
+    Ts = w.T
+    probe_T = min(w.T, 256)
+    t0 = time.perf_counter()
+    oracle.recurrence(inp.q[:, :probe_T], inp.k[:, :probe_T], inp.v[:, :probe_T],
+                      inp.g[:, :probe_T], inp.beta[:, :probe_T], inp.scale,
+                      inp.s0, threads=threads)
+    rate = probe_T / max(time.perf_counter() - t0, 1e-9)     # token positions / s
+    if w.T / rate > budget_s:
+        Ts = max(probe_T, int(rate * budget_s))
+    reps, spent, tokens = 0, 0.0, 0
+    while spent < budget_s * 0.5 or reps == 0:
+        t0 = time.perf_counter()
+        oracle.recurrence(inp.q[:, :Ts], inp.k[:, :Ts], inp.v[:, :Ts], inp.g[:, :Ts],
+                          inp.beta[:, :Ts], inp.scale, inp.s0, threads=threads)
+        spent += time.perf_counter() - t0
+        tokens += w.B * Ts
+        reps += 1
+    sample = (f"fp64 recurrence on all {w.B * w.HV} (batch, value head) scans, "
+              f"{'all' if Ts == w.T else 'first'} {Ts} of {w.T} tokens, x{reps} passes, "
+              f"{spent:.1f} s")
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample}
+
+
+def copy_calibration(mib, reps):
+    """Plain device copy of known size, for scaling rocprof FETCH/WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD_DEFAULT)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating input/output copies (0: enough to exceed 640 MiB)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs the forward pass on one GPU; there is no "
+              "multi-GPU path to measure (heads and batches shard across GPUs with no "
+              "communication; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calib_copy_mib:
+        copy_calibration(args.calib_copy_mib, max(args.steps, 1))
+        return
+
+    import chunkwise_gated_delta_cumsum_amd as gdr
+    from chunkwise_gated_delta_cumsum_amd.inputs import make_inputs, workload
+
+    gdr.load()
+    w = workload(args.workload)
+    inp = make_inputs(w)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base = dict(q=to_dev(inp.q_dev), k=to_dev(inp.k_dev), v=to_dev(inp.v_dev),
+                g=to_dev(inp.g), beta=to_dev(inp.beta),
+                s0=None if inp.s0 is None else to_dev(inp.s0))
+    prob = gdr.problem(w.B, w.T, w.H, w.HV, w.K, w.V, chunk=w.chunk,
+                       per_channel=w.per_channel, scale=inp.scale, dtype=w.dtype)
+    ws_bytes = gdr.workspace_size(prob)
+    per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    per_set += ws_bytes + w.B * w.T * w.HV * w.V * 4 + w.B * w.HV * w.K * w.V * 4
+    nsets = args.sets or max(1, -(-(640 << 20) // per_set))
+    sets = []
+    for i in range(nsets):
+        d = base if i == 0 else {k_: (None if t is None else t.clone()) for k_, t in base.items()}
+        d = dict(d)
+        d["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        d["o"] = torch.empty((w.B, w.T, w.HV, w.V), dtype=torch.float32, device=dev)
+        d["sT"] = torch.empty((w.B, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+        sets.append(d)
+
+    def step(d, e0=None, e1=None, e2=None):
+        if e0 is not None:
+            e0.record()
+        gdr.gdr_chunk_prep(d["q"], d["k"], d["g"], d["beta"], chunk=w.chunk, scale=inp.scale,
+                           V=w.V, workspace=d["ws"])
+        if e1 is not None:
+            e1.record()
+        gdr.gdr_chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["ws"], d["s0"],
+                           chunk=w.chunk, scale=inp.scale, out=(d["o"], d["sT"]))
+        if e2 is not None:
+            e2.record()
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % nsets], *evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+
+    # the path check: one more pass through the single-call entry point
+    d = sets[0]
+    o_ref = d["o"].clone()
+    gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk=w.chunk,
+                      scale=inp.scale, workspace=d["ws"], out=(d["o"], d["sT"]))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o_ref, d["o"]))
+
+    tm = traffic_model(w)
+    kern = {"chunk_prep_kernel": (prep_ms, tm["prep"]), "chunk_scan_kernel": (scan_ms, tm["scan"])}
+    dom = max(kern, key=lambda k_: kern[k_][0])
+    dom_ms, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    ms_per_step = elapsed / K * 1e3
+    tokens = w.B * w.T
+    flops = algorithmic_flops(w)
+    mfma_peak = MFMA_F32_PEAK_TFLOPS if w.dtype == "fp32" else MFMA_F16_PEAK_TFLOPS
+
+    rec = {
+        "metric": "tokens/sec of chunked gated-delta-rule fwd at 1 GPU; % HBM/MFMA roofline",
+        "value": tokens / (elapsed / K),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "fp32" else "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K,
+                   "V": w.V, "chunk": w.chunk,
+                   "decay": "per-channel" if w.per_channel else "scalar",
+                   "inputs": w.dtype, "initial_state": w.s0_std > 0,
+                   "accumulate": "fp32", "rotating_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "kernel_ms": {"chunk_prep_kernel": prep_ms, "chunk_scan_kernel": scan_ms},
+                     "path_compulsory_bytes": tm["compulsory"],
+                     "path_hbm_frac": tm["compulsory"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak},
+        "fwd_entry_point_matches": same,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -218,8 +218,11 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
 
 
 def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 64,
-                   scale: Optional[float] = None):
-    """Run the state-scan stage on a workspace filled by gdr_chunk_prep."""
+                   scale: Optional[float] = None, *, out=None):
+    """Run the state-scan stage on a workspace filled by gdr_chunk_prep.
+
+    ``out`` = (o, final_state) reuses caller tensors (final_state may be None).
+    """
     import torch
     lib = load()
     dev = q.device
@@ -227,8 +230,11 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
     prob = _problem_from(q, k, v, g, beta, chunk, scale)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
-    o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
-    s = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
+    if out is not None:
+        o, s = out
+    else:
+        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+        s = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     st = lib.gdr_chunk_scan(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(initial_state),
                             _ptr(o), _ptr(s), _ptr(workspace), workspace.numel(), _stream(dev))
     check(st)
