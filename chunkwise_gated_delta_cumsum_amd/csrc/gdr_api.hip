@@ -19,14 +19,45 @@ using namespace gdr;
 
 namespace {
 
-constexpr int kScanBV = 32;  // value columns per scan workgroup (16 per wave)
-
 struct Prob {
   int B, T, H, HV, K, V, N;
   bool perch, f32;
   float scale;
-  size_t es;  // bytes per q/k/v element and per workspace fragment element
+  size_t es;        // bytes per q/k/v element and per workspace fragment element
+  int nseg, seg_len; // sequence segments of the state scan
 };
+
+// Number of sequence segments for the state scan.  One segment runs the
+// serial scan over all N chunks with B*HV*V/64 workgroups.  P segments run a
+// chain pass (B*HV*(P-1)*(K+V)/64 workgroups, seg_len chunks each, about 0.6
+// of a full chunk step), a serial combine (P-1 steps, about 0.5 each) and the
+// full pass (B*HV*P*V/64 workgroups, seg_len chunks).  Workgroups beyond the
+// 256 compute units of an MI355X run in further rounds.  The estimate uses
+// problem sizes only, so the workspace size query needs no device query.
+int choose_segments(int BH, int N, int K, int V, int& seg_len) {
+  // chain workgroups fit two per compute unit, full ones one
+  constexpr double kCU = 256.0, kChainSlots = 512.0, kChain = 0.6, kComb = 0.5, kLaunch = 2.0;
+  double best = 1e300;
+  int bestP = 1;
+  seg_len = N;
+  for (int P = 1; P <= 256 && P <= N; ++P) {
+    const int L = (N + P - 1) / P;
+    const int Pe = (N + L - 1) / L;
+    if (Pe != P) continue;
+    const double r3 = std::ceil((double)BH * P * (V / 64) / kCU);
+    double t = r3 * L;
+    if (P > 1) {
+      const double r1 = std::ceil((double)BH * (P - 1) * ((K + V) / 64) / kChainSlots);
+      t += r1 * L * kChain + (P - 1) * kComb + 2 * kLaunch;
+    }
+    if (t < best * 0.999) {
+      best = t;
+      bestP = P;
+      seg_len = L;
+    }
+  }
+  return bestP;
+}
 
 gdr_status validate(const gdr_problem* p, Prob* out) {
   if (!p) return GDR_ERR_NULL;
@@ -45,15 +76,26 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.f32 = p->qkv_dtype == GDR_F32;
   r.scale = p->scale;
   r.es = r.f32 ? 4 : 2;
+  if (p->scan_segments < 0) return GDR_ERR_ARG;
+  if (p->scan_segments == 0) {
+    r.nseg = choose_segments(r.B * r.HV, r.N, r.K, r.V, r.seg_len);
+  } else {
+    const int want = p->scan_segments < r.N ? p->scan_segments : r.N;
+    r.seg_len = (r.N + want - 1) / want;
+    r.nseg = (r.N + r.seg_len - 1) / r.seg_len;
+  }
   // grid sizes must fit a 32-bit launch dimension
-  if ((uint64_t)r.B * r.HV * r.N > 0x7fffffffull) return GDR_ERR_SHAPE;
+  if ((uint64_t)r.B * r.HV * r.N + 8ull * r.HV > 0x7fffffffull) return GDR_ERR_SHAPE;
   if (out) *out = r;
   return GDR_OK;
 }
 
 size_t nchunks(const Prob& r) { return (size_t)r.B * r.HV * r.N; }
 
-WsLayout layout(const Prob& r) { return ws_layout(nchunks(r), r.K, r.perch, r.es); }
+WsLayout layout(const Prob& r) {
+  const size_t qk = r.perch ? nchunks(r) : (size_t)r.B * r.H * r.N;
+  return ws_layout(nchunks(r), qk, r.K, r.V, r.es, (size_t)r.B * r.HV, r.nseg);
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -122,7 +164,10 @@ gdr_status launch(Kern kern, unsigned grid, unsigned block, Args& args, hipStrea
 
 template <int K, bool PERCH, class P>
 gdr_status launch_prep_k(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
-  const unsigned grid = (unsigned)nchunks(r);
+  // (batch, q/k head, chunk) units rounded up to the 8 XCDs, times the
+  // value heads of each q/k head; surplus workgroups exit
+  const size_t units8 = ((size_t)r.B * r.H * r.N + 7) / 8 * 8;
+  const unsigned grid = (unsigned)(units8 * (r.HV / r.H));
   if (dump) return launch(chunk_prep_kernel<K, PERCH, P, true>, grid, 256, a, s);
   return launch(chunk_prep_kernel<K, PERCH, P, false>, grid, 256, a, s);
 }
@@ -143,9 +188,21 @@ gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
 
 template <int K, int V, bool PERCH, class P>
 gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
-  constexpr int BV = kScanBV;
-  const unsigned grid = (unsigned)((size_t)r.B * r.HV * (V / BV));
-  return launch(chunk_scan_kernel<K, V, BV, PERCH, P>, grid, BV / 16 * 64, a, s);
+  const size_t BH = (size_t)r.B * r.HV;
+  auto grid_for = [](size_t units, int nslab) {
+    // units rounded up to a multiple of the 8 XCDs; surplus workgroups exit
+    return (unsigned)((units + 7) / 8 * 8 * nslab);
+  };
+  gdr_status st;
+  if (r.nseg > 1) {
+    st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain>,
+                grid_for(BH * (r.nseg - 1), (K + V) / kScanBV), kScanWaves * 64, a, s);
+    if (st != GDR_OK) return st;
+    st = launch(seg_combine_kernel<K, V, P>, grid_for(BH, V / kScanBV), kScanWaves * 64, a, s);
+    if (st != GDR_OK) return st;
+  }
+  return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull>,
+                grid_for(BH * r.nseg, V / kScanBV), kScanWaves * 64, a, s);
 }
 
 template <bool PERCH, class P>
@@ -182,13 +239,17 @@ PrepArgs prep_args(const Prob& r, const void* q, const void* k, const float* g,
 ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
                    const float* s0, float* o, float* sT, const void* ws) {
   const WsLayout L = layout(r);
-  const char* base = static_cast<const char*>(ws);
+  char* base = static_cast<char*>(const_cast<void*>(ws));
   ScanArgs a;
   a.q = q; a.k = k; a.v = v; a.s0 = s0; a.o = o; a.sT = sT;
   a.wt = base + L.wt; a.ah = base + L.ah; a.rs = reinterpret_cast<const float*>(base + L.rs);
   a.qh = base + L.qh; a.kh = base + L.kh;
   a.B = r.B; a.T = r.T; a.H = r.H; a.HV = r.HV; a.N = r.N;
   a.scale = r.scale;
+  a.seg_len = r.seg_len; a.nseg = r.nseg;
+  a.seg_state = reinterpret_cast<float*>(base + L.seg);
+  a.phi = reinterpret_cast<float*>(base + L.phi);
+  a.eend = reinterpret_cast<float*>(base + L.eend);
   return a;
 }
 
@@ -272,7 +333,7 @@ gdr_status gdr_chunk_prep(const gdr_problem* p, const void* q, const void* k, co
 
 gdr_status gdr_chunk_scan(const gdr_problem* p, const void* q, const void* k, const void* v,
                           const float* initial_state, float* o, float* final_state,
-                          const void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream) {
   Prob r;
   gdr_status st = validate(p, &r);
   if (st != GDR_OK) return st;
@@ -285,6 +346,7 @@ gdr_status gdr_chunk_scan(const gdr_problem* p, const void* q, const void* k, co
                         workspace, workspace_bytes);
   if (out_overlaps(s.o, {s.q, s.k, s.v, s.s0, s.sT, s.ws})) return GDR_ERR_ALIAS;
   if (out_overlaps(s.sT, {s.q, s.k, s.v, s.ws})) return GDR_ERR_ALIAS;
+  if (out_overlaps(s.ws, {s.q, s.k, s.v, s.s0})) return GDR_ERR_ALIAS;
   if (initial_state && final_state && initial_state != final_state && overlap(s.sT, s.s0))
     return GDR_ERR_ALIAS;
   if ((st = check_device()) != GDR_OK) return st;
@@ -303,10 +365,16 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace NULL or smaller than gdr_chunk_fwd_workspace_size";
     case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE: the current HIP device is not gfx950";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP query or kernel launch failed";
-    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite and g_per_channel 0 or 1";
+    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel 0 or 1, scan_segments >= 0";
     case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: an output overlaps an input or another output";
     default: return "GDR_ERR_UNKNOWN: unknown status value";
   }
+}
+
+int gdr_chunk_scan_segments(const gdr_problem* p) {
+  Prob r;
+  if (validate(p, &r) != GDR_OK) return 0;
+  return r.nseg;
 }
 
 int gdr_version(void) { return 100; }

@@ -66,8 +66,30 @@ struct PolicyF16 {
   using in_t = uint16_t;   // bf16 bits
   using frag_t = half8;
   using ws_t = _Float16;
+  using raw_t = u16x8;     // 8 input elements as loaded, before conversion
   static constexpr bool kF32 = false;
+  __device__ static __forceinline__ raw_t load_raw(const in_t* row, int grp) {
+    const u16x4 lo = *reinterpret_cast<const u16x4*>(row + 4 * grp);
+    const u16x4 hi = *reinterpret_cast<const u16x4*>(row + 16 + 4 * grp);
+    return raw_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  // convert raw input elements to a fragment; zero when !valid
+  __device__ static __forceinline__ frag_t from_raw(raw_t x, bool valid) {
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = valid ? (_Float16)bf16_to_f32(x[i]) : (_Float16)0.f;
+    return f;
+  }
   __device__ static __forceinline__ float in_to_f32(in_t x) { return bf16_to_f32(x); }
+  __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return bf16_to_f32(x[i]); }
+  // 16x16 tile += (16 x 16) * (16 x 16), lane holds k = 4*grp + i; fp16
+  // operands (the inverse is consumed as fp16 anyway), fp32 accumulation
+  __device__ static __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 ah = {(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+    const h4 bh = {(_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(ah, bh, c, 0, 0, 0);
+  }
   __device__ static __forceinline__ frag_t make(const float* v) {
     frag_t f;
 #pragma unroll
@@ -86,8 +108,24 @@ struct PolicyF32 {
   using in_t = float;
   using frag_t = f32x8;
   using ws_t = float;
+  using raw_t = f32x8;
   static constexpr bool kF32 = true;
+  __device__ static __forceinline__ raw_t load_raw(const in_t* row, int grp) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 + 4 * grp);
+    return raw_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static __forceinline__ frag_t from_raw(raw_t x, bool valid) {
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = valid ? x[i] : 0.f;
+    return f;
+  }
   __device__ static __forceinline__ float in_to_f32(in_t x) { return x; }
+  __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return x[i]; }
+  __device__ static __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {
+    return mma16_f32(a, b, c);
+  }
   __device__ static __forceinline__ frag_t make(const float* v) {
     frag_t f;
 #pragma unroll
@@ -185,25 +223,35 @@ __device__ __forceinline__ void store_ws8(float* p, const float* v) {
 //   ah : A^ = A_qk M^-1 as an A operand (rows i, k = c): [4][2][64][8]
 //   rs : 256 fp32: [0..63] exp(gamma_c) (one decay per row; 1 per channel),
 //        [64..64+K) exp(gamma_last) per key channel
-//   qh, kh (per-channel decay only): q exp(gamma) scale and k exp(gamma) as A
-//        operands (rows c, k = d): [4][K/32][64][8]
+//   qh, kh : q and k as A operands (rows c, k = d): [4][K/32][64][8].  With
+//        one decay per row they are the raw inputs, stored once per (batch,
+//        q/k head, chunk); with per-channel decay they are q exp(gamma) scale
+//        and k exp(gamma), stored per value head.
+//   seg, phi, eend : sequence segments (when more than one): start states
+//        [B*HV][nseg][K*V], transitions [B*HV][nseg-1][K][K] and zero-start end
+//        states [B*HV][nseg-1][K*V], fp32.
 struct WsLayout {
-  size_t wt, ah, rs, qh, kh, total;
+  size_t wt, ah, rs, qh, kh, seg, phi, eend, total;
 };
 
 __host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__host__ __device__ inline WsLayout ws_layout(size_t nchunks, int K, bool per_channel,
-                                              size_t elem) {
+// nchunks = B * HV * N value-head chunks; qkchunks = chunks that carry their
+// own q/k fragments (B * H * N with one decay per row, nchunks per channel).
+__host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, int K, int V,
+                                              size_t elem, size_t nheads, int nseg) {
   WsLayout L;
   size_t off = 0;
   L.wt = off; off = ws_align(off + nchunks * (size_t)K * kChunk * elem);
   L.ah = off; off = ws_align(off + nchunks * (size_t)kChunk * kChunk * elem);
   L.rs = off; off = ws_align(off + nchunks * 256 * sizeof(float));
-  L.qh = L.kh = off;
-  if (per_channel) {
-    L.qh = off; off = ws_align(off + nchunks * (size_t)kChunk * K * elem);
-    L.kh = off; off = ws_align(off + nchunks * (size_t)kChunk * K * elem);
+  L.qh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
+  L.kh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
+  L.seg = L.phi = L.eend = off;
+  if (nseg > 1) {
+    L.seg = off; off = ws_align(off + nheads * nseg * (size_t)K * V * sizeof(float));
+    L.phi = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * K * sizeof(float));
+    L.eend = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * V * sizeof(float));
   }
   L.total = off;
   return L;

@@ -27,8 +27,10 @@
  *   final_state    [B, HV, K, V]   fp32 (output), or NULL to skip
  *
  * Ownership: the caller allocates and owns every buffer, the workspace
- * included.  The library never allocates or frees device memory and keeps
- * no mutable global state; calls on different streams are independent.
+ * included.  The library never allocates or frees device memory; its only
+ * global state is a per-device cache of the architecture check.  Calls on
+ * different streams are independent when they use different workspaces and
+ * outputs.
  *
  * Streams: work is enqueued asynchronously on `stream` (a hipStream_t; NULL
  * is the null stream).  No call synchronises.  A fault inside a kernel shows
@@ -76,6 +78,10 @@ typedef struct gdr_problem {
   int32_t g_per_channel;     /* 0: g[B,T,HV]; 1: g[B,T,HV,K] */
   float scale;               /* query scale; callers usually pass 1/sqrt(K) */
   int32_t qkv_dtype;         /* gdr_dtype of q, k and v */
+  int32_t scan_segments;     /* sequence segments of the state scan: 0 chooses
+                                automatically (gdr_chunk_scan_segments), n > 0
+                                asks for n (rounded so that every segment holds
+                                the same number of chunks, at most one per chunk) */
 } gdr_problem;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when
@@ -113,17 +119,29 @@ gdr_status gdr_chunk_prep(const gdr_problem* p,
                           float* gamma, float* a_kk, float* a_qk, float* m_inv,
                           void* stream);
 
-/* Stage 2 alone (sec-03 notes, inter-chunk recurrence): the serial scan over
+/* Stage 2 alone (sec-03 notes, inter-chunk recurrence): the scan over
  * chunks using a workspace filled by gdr_chunk_prep for the same problem and
  * the same q, k, g, beta.  r = U - W S, o = (q exp(gamma)) S + A_qk r,
  * S <- diag(exp(gamma_last)) S + (exp(gamma_last - gamma) k)^T (beta r),
- * with W = M^-1 (exp(gamma) k) and U = M^-1 v folded into the workspace. */
+ * with W = M^-1 (exp(gamma) k) and U = M^-1 v folded into the workspace.
+ * When the problem has few independent (batch, value head) scans relative to
+ * its length, the sequence is cut into segments: the state update is affine
+ * in S, so each segment's transition and zero-start end state are computed
+ * in parallel, combined serially, and the segments then rerun from their
+ * true start states.  Those segment states are written into the workspace,
+ * which this stage therefore also writes. */
 gdr_status gdr_chunk_scan(const gdr_problem* p,
                           const void* q, const void* k, const void* v,
                           const float* initial_state,
                           float* o, float* final_state,
-                          const void* workspace, size_t workspace_bytes,
+                          void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Number of sequence segments the state scan of problem `p` uses (1: one
+ * serial scan over all chunks), or 0 when `p` fails validation.  The
+ * automatic choice comes from a cost model of the MI355X (256 compute
+ * units) and the problem sizes only. */
+int gdr_chunk_scan_segments(const gdr_problem* p);
 
 /* Static, never-NULL text for any status value (unknown values included). */
 const char* gdr_status_string(int status);

@@ -157,3 +157,20 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         binding.load()
+
+
+def test_scan_segment_query(lib):
+    p = base(T=4096, H=12, HV=12)
+    auto = gdr.scan_segments(p)
+    assert auto >= 1
+    for want, N in ((1, 64), (3, 64), (64, 64), (1000, 64)):
+        q = base(T=64 * N, H=12, HV=12, segments=want)
+        got = gdr.scan_segments(q)
+        L = -(-N // min(want, N))
+        assert got == -(-N // L)
+        assert gdr.workspace_size(q) > 0
+    bad = base(segments=-1)
+    assert gdr.scan_segments(bad) == 0
+    assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"
+    # more segments need more workspace (transitions and states)
+    assert gdr.workspace_size(base(T=4096, segments=8)) > gdr.workspace_size(base(T=4096, segments=1))
