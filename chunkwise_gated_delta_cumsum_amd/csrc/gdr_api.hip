@@ -12,7 +12,7 @@
 
 #include "gdr.h"
 #include "gdr_device.hpp"
-#include "gdr_prep.hpp"
+#include "gdr_prep_kda.hpp"
 #include "gdr_scan.hpp"
 
 using namespace gdr;
@@ -168,8 +168,13 @@ gdr_status launch_prep_k(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
   // value heads of each q/k head; surplus workgroups exit
   const size_t units8 = ((size_t)r.B * r.H * r.N + 7) / 8 * 8;
   const unsigned grid = (unsigned)(units8 * (r.HV / r.H));
-  if (dump) return launch(chunk_prep_kernel<K, PERCH, P, true>, grid, 256, a, s);
-  return launch(chunk_prep_kernel<K, PERCH, P, false>, grid, 256, a, s);
+  if constexpr (PERCH) {
+    if (dump) return launch(chunk_prep_kda_kernel<K, P, true>, grid, 256, a, s);
+    return launch(chunk_prep_kda_kernel<K, P, false>, grid, 256, a, s);
+  } else {
+    if (dump) return launch(chunk_prep_kernel<K, P, true>, grid, 256, a, s);
+    return launch(chunk_prep_kernel<K, P, false>, grid, 256, a, s);
+  }
 }
 
 template <bool PERCH, class P>

@@ -215,6 +215,14 @@ __device__ __forceinline__ void store_ws8(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+__device__ __forceinline__ void store_ws4(_Float16* p, const float* v) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<h4*>(p) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+}
+__device__ __forceinline__ void store_ws4(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
 // ---- workspace layout -----------------------------------------------------
 // Per chunk (one value head, C = 64 rows), in fragment order so every lane
 // reads or writes 8 consecutive elements:

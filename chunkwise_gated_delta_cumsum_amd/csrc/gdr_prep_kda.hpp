@@ -1,0 +1,346 @@
+// Chunk preparation with one decay per key channel (the KDA form of the
+// "Chunkwise parallel algorithms" page and the sec-03 notes' per-channel
+// decay).  Same outputs as chunk_prep_kernel, but gamma is a C x K matrix,
+// so the decay cannot be pulled out of the Gram products: it must be folded
+// into their operands, exp(gamma_i - gamma_j) = f(i) f'(j) per channel, with
+// every factor kept in range.
+//
+// Wave I owns the rows of block I (rows 16I..16I+15); lane (r, grp) holds row
+// 16I + r at the channels kslot(grp, .) of every 32-channel group, in
+// registers, from the global loads on.  Per chunk:
+//   1. s = in-block inclusive cumsum of g (a DPP scan across the 16 lanes of
+//      a row), block totals to LDS; gamma_i = pre[I] + s_i with pre[m] the
+//      sum of the totals of the blocks before m.
+//   2. Off-diagonal tiles (I > J) factor the decay about the block edges:
+//        exp(g_i - g_j) = exp(s_i) * exp(pre[I] - pre[J+1]) * exp(s15_J - s_j)
+//      (g = gamma here).  With g <= 0 every factor is at most 1, so nothing
+//      overflows; underflow only hits entries that are themselves below the
+//      fp16 range.  The first factor goes on the later row (register
+//      fragments of block I), the other two on the earlier row (block J's
+//      fragment, shared through LDS, times a per-channel table).
+//   3. Diagonal tiles factor about the block's middle row m in fp32,
+//      exp(s_i - s_m) exp(s_m - s_j), on fp32 MFMA; exact while |s - s_m| <=
+//      80 on the block.  Beyond that (decays near e^-80 within 8 rows) the
+//      wave sums the 16x16 entries explicitly, exp per channel and entry.
+//   4. q exp(gamma) scale and k exp(gamma) (the scan's operands) and
+//      beta k exp(gamma_last - gamma) (for W^) from the same factors and the
+//      per-block tables exp(pre[I]) and exp(pre[4] - pre[I+1]).
+// Steps 3-4 of the UT transform (inverse and folding) are shared with the
+// scalar kernel.  With g > 0 the factors grow as exp(sum of the positive g in
+// the chunk); fp16 operands stay finite while that sum is below about 8.
+#pragma once
+#include "gdr_prep.hpp"
+
+namespace gdr {
+
+// Threshold of the fp32 middle-row factorisation of a diagonal block.
+constexpr float kDiagExpLimit = 80.f;
+
+// Inclusive scan across the 16 lanes of each DPP row (lanes 16g .. 16g+15).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  // lanes whose source would lie before the row start read 0
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_scan16(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
+template <int K, class P, bool DUMP>
+__global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
+  using in_t = typename P::in_t;
+  using frag_t = typename P::frag_t;
+  using ws_t = typename P::ws_t;
+  using raw_t = typename P::raw_t;
+  constexpr int C = kChunk;
+  constexpr int KB = K / 32;
+  constexpr int LP = kLP;
+  constexpr int SP = K + 16 / (int)sizeof(ws_t);   // row of the W^ operand tile, +16 bytes
+  constexpr int NPAIR = 6;                          // off-diagonal block pairs J < I
+
+  constexpr size_t KE_BYTES = (size_t)3 * KB * 64 * sizeof(frag_t);
+  constexpr size_t TAB_BYTES = (size_t)(4 + 4 + NPAIR) * K * sizeof(float);
+  constexpr size_t MT_BYTES = (size_t)C * LP * sizeof(float);
+  constexpr size_t X_BYTES = KE_BYTES + TAB_BYTES > MT_BYTES ? KE_BYTES + TAB_BYTES : MT_BYTES;
+  // earlier-row fragments of blocks 0..2 and the per-channel tables; M^-T later
+  __shared__ __attribute__((aligned(16))) char sX[X_BYTES];
+  // beta k exp(gamma_last - gamma), row-major (c, d), for W^
+  __shared__ __attribute__((aligned(16))) ws_t sSK[C * SP];
+  __shared__ __attribute__((aligned(16))) float sL[C * LP];    // A_kk beta (strict); D_I later
+  __shared__ __attribute__((aligned(16))) float sTot[4 * K];   // s at row 15 of each block
+  __shared__ __attribute__((aligned(16))) float sMid[4 * K];   // s at row 7 of each block
+  __shared__ float sBeta[C];
+  frag_t* sKE = reinterpret_cast<frag_t*>(sX);                  // [3][KB][64]
+  float* sPf = reinterpret_cast<float*>(sX + KE_BYTES);         // [4][K] exp(pre[I])
+  float* sSf = sPf + 4 * K;                                      // [4][K] exp(pre[4] - pre[I+1])
+  float* sCf = sSf + 4 * K;                                      // [6][K] exp(pre[I] - pre[J+1])
+  float* sMT = reinterpret_cast<float*>(sX);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  int b, hv, n;
+  if (!prep_block(a.B, a.H, a.HV / a.H, a.N, b, hv, n)) return;
+  const int h = hv / (a.HV / a.H);
+  const int cid = (b * a.HV + hv) * a.N + n;
+  const int T = a.T;
+  const int I = wave;
+  const int i = 16 * I + r;                 // this lane's row in the chunk
+  const int t = n * C + i;
+  const bool valid = t < T;
+  GDR_PPROF(0);
+
+  // ---- loads: this lane's row, channels 32kb + kslot(grp, .) ---------------
+  raw_t qr[KB], kr[KB];
+  f32x4 glo[KB], ghi[KB];
+  float bv;
+  {
+    const int tt = min(t, T - 1);
+    const in_t* qrow = static_cast<const in_t*>(a.q) + (((size_t)b * T + tt) * a.H + h) * K;
+    const in_t* krow = static_cast<const in_t*>(a.k) + (((size_t)b * T + tt) * a.H + h) * K;
+    const float* grow = a.g + (((size_t)b * T + tt) * a.HV + hv) * K;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qr[kb] = P::load_raw(qrow + 32 * kb, grp);
+      kr[kb] = P::load_raw(krow + 32 * kb, grp);
+      glo[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 4 * grp);
+      ghi[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 16 + 4 * grp);
+    }
+    bv = a.beta[((size_t)b * T + tt) * a.HV + hv];
+  }
+  if (!valid) bv = 0.f;
+
+  // ---- 1. in-block cumsum ----------------------------------------------------
+  float s[KB][8];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[kb][j] = row_scan16(valid ? glo[kb][j] : 0.f);
+      s[kb][4 + j] = row_scan16(valid ? ghi[kb][j] : 0.f);
+    }
+  if (r == 15 || r == 7) {
+    float* dst = (r == 15 ? sTot : sMid) + I * K;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      *reinterpret_cast<f32x4*>(dst + 32 * kb + 4 * grp) = f32x4{s[kb][0], s[kb][1], s[kb][2], s[kb][3]};
+      *reinterpret_cast<f32x4*>(dst + 32 * kb + 16 + 4 * grp) = f32x4{s[kb][4], s[kb][5], s[kb][6], s[kb][7]};
+    }
+  }
+  if (grp == 0) sBeta[i] = bv;
+  __syncthreads();
+  GDR_PPROF(1);
+
+  // ---- per-channel tables (all threads) --------------------------------------
+  {
+    const int d = tid % K, part = tid / K;
+    float pre[5];
+    pre[0] = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pre[m + 1] = pre[m] + sTot[m * K + d];
+    float* rs = a.rs + (size_t)cid * 256;
+    for (int it = part; it < 15; it += 256 / K) {
+      if (it < 4) {
+        sPf[it * K + d] = __expf(pre[it]);
+      } else if (it < 8) {
+        sSf[(it - 4) * K + d] = __expf(pre[4] - pre[it - 3]);
+      } else if (it < 14) {
+        const int p = it - 8, I2 = p < 1 ? 1 : (p < 3 ? 2 : 3), J2 = p - I2 * (I2 - 1) / 2;
+        sCf[p * K + d] = __expf(pre[I2] - pre[J2 + 1]);
+      } else {
+        rs[64 + d] = __expf(pre[4]);
+      }
+    }
+    if (tid < C) rs[tid] = 1.f;
+  }
+
+  // ---- 2/3. own-block factors, earlier-row fragments, diagonal tiles ----------
+  // kl = k exp(s), ql = q exp(s): the later-row side (reference row 16I - 1);
+  // ke = k exp(s15 - s): the earlier-row side (reference row 16I + 15).
+  float kl[KB][8], ql[KB][8], ke[KB][8];
+  f32x4 dkk = zero4(), dqk = zero4();      // diagonal A_kk and A_qk^T tiles (raw dots)
+  bool far = false;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const f32x4 t15a = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 4 * grp);
+    const f32x4 t15b = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 16 + 4 * grp);
+    const f32x4 tma = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 4 * grp);
+    const f32x4 tmb = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 16 + 4 * grp);
+    float a1[8], b1[8], b2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float s15 = j < 4 ? t15a[j] : t15b[j - 4];
+      const float sm = j < 4 ? tma[j] : tmb[j - 4];
+      const float x = s[kb][j];
+      const float qv = valid ? P::raw_f32(qr[kb], j) : 0.f;
+      const float kv = valid ? P::raw_f32(kr[kb], j) : 0.f;
+      const float el = __expf(x);
+      kl[kb][j] = kv * el;
+      ql[kb][j] = qv * el;
+      ke[kb][j] = kv * __expf(s15 - x);
+      const float dl = x - sm;
+      far |= !(fabsf(dl) <= kDiagExpLimit);
+      const float dm = __expf(dl), dmi = __expf(-dl);
+      a1[j] = kv * dm;
+      b1[j] = kv * dmi;
+      b2[j] = qv * dm;
+    }
+    if (I < 3) sKE[(I * KB + kb) * 64 + lane] = P::make(ke[kb]);
+    const f32x8 fa1 = {a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]};
+    const f32x8 fb1 = {b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]};
+    const f32x8 fb2 = {b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]};
+    dkk = mma32(fa1, fb1, dkk);   // rows i, columns j of block I
+    dqk = mma32(fb1, fb2, dqk);   // rows c' (k), columns i (q) of block I
+  }
+  if (__any(far)) {
+    // Explicit diagonal block: lane (r, grp) sums its channels for the pairs
+    // (row r, row (r - m) mod 16), m = 0..15, the four channel groups are
+    // added across lanes, and the entries are routed through LDS (the W^
+    // tile is not written yet) into accumulator layout.
+    float* scr = reinterpret_cast<float*>(sSK) + wave * 512;   // [2][16][16]
+    for (int m = 0; m < 16; ++m) {
+      const int jr = (r - m) & 15;
+      const int src = jr + 16 * grp;
+      float pk = 0.f, pq = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float qv = valid ? P::raw_f32(qr[kb], j) : 0.f;
+          const float kv = valid ? P::raw_f32(kr[kb], j) : 0.f;
+          const float kj = __shfl(kv, src, 64);
+          const float sj = __shfl(s[kb][j], src, 64);
+          const float e = __expf(s[kb][j] - sj);
+          pk += kv * kj * e;
+          pq += qv * kj * e;
+        }
+      pk += __shfl_xor(pk, 16, 64);
+      pk += __shfl_xor(pk, 32, 64);
+      pq += __shfl_xor(pq, 16, 64);
+      pq += __shfl_xor(pq, 32, 64);
+      if (grp == 0 && jr <= r) {
+        scr[r * 16 + jr] = pk;          // A_kk (i = r, j = jr)
+        scr[256 + jr * 16 + r] = pq;    // A_qk^T (c' = jr, i = r)
+      }
+    }
+    // the wave's own LDS writes are complete before it reads them back
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int rr = 4 * grp + j4;
+      dkk[j4] = rr > r ? scr[rr * 16 + r] : 0.f;
+      dqk[j4] = rr <= r ? scr[256 + rr * 16 + r] : 0.f;
+    }
+  }
+  if constexpr (DUMP) {
+    if (a.d_gamma) {
+      float* dg = a.d_gamma + ((size_t)cid * C + i) * K;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int d = 32 * kb + kslot(grp, j);
+          float pre = 0.f;
+          for (int m = 0; m < I; ++m) pre += sTot[m * K + d];
+          dg[d] = pre + s[kb][j];
+        }
+    }
+  }
+  __syncthreads();   // sKE and the tables are complete; the scratch is read
+  GDR_PPROF(2);
+
+  // ---- off-diagonal tiles (J < I) ----------------------------------------------
+  f32x4 aqT[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aqT[j] = zero4();
+  if (I > 0) {
+    frag_t kLf[KB], qLf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      kLf[kb] = P::make(kl[kb]);
+      qLf[kb] = P::make(ql[kb]);
+    }
+    for (int J = 0; J < I; ++J) {
+      const float* cf = sCf + (I * (I - 1) / 2 + J) * K;
+      f32x4 akk = zero4(), aq = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const frag_t fe = sKE[(J * KB + kb) * 64 + lane];
+        const f32x4 ca = *reinterpret_cast<const f32x4*>(cf + 32 * kb + 4 * grp);
+        const f32x4 cb = *reinterpret_cast<const f32x4*>(cf + 32 * kb + 16 + 4 * grp);
+        float fv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fv[j] = (float)fe[j] * (j < 4 ? ca[j] : cb[j - 4]);
+        const frag_t F = P::make(fv);
+        akk = mma32(kLf[kb], F, akk);   // rows i (block I), columns j (block J)
+        aq = mma32(F, qLf[kb], aq);     // rows c' (block J), columns i (block I)
+      }
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int ii = 16 * I + 4 * grp + j4, jj = 16 * J + r;
+        sL[ii * LP + jj] = akk[j4] * sBeta[jj];
+        aq[j4] *= sBeta[16 * J + 4 * grp + j4] * a.scale;
+      }
+      aqT[J] = aq;
+    }
+  }
+  // diagonal tiles: masks, beta, scale
+#pragma unroll
+  for (int j4 = 0; j4 < 4; ++j4) {
+    const int rr = 16 * I + 4 * grp + j4, cc = 16 * I + r;
+    sL[rr * LP + cc] = rr > cc ? dkk[j4] * sBeta[cc] : 0.f;
+    aqT[I][j4] = rr <= cc ? dqk[j4] * sBeta[rr] * a.scale : 0.f;
+  }
+
+  // ---- scan operands and the W^ operand ----------------------------------------
+  {
+    const size_t off0 = (size_t)cid * 4 * KB * 512 + ((size_t)I * KB) * 512 + lane * 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int d0 = 32 * kb + 4 * grp;
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(sPf + I * K + d0);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(sPf + I * K + d0 + 16);
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(sSf + I * K + d0);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(sSf + I * K + d0 + 16);
+      float qx[8], kx[8], wx[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pf = j < 4 ? pa[j] : pb[j - 4];     // exp(gamma_i) = exp(s) exp(pre[I])
+        qx[j] = ql[kb][j] * pf * a.scale;
+        kx[j] = kl[kb][j] * pf;
+        // exp(gamma_last - gamma_i) = exp(s15 - s) exp(pre[4] - pre[I+1])
+        wx[j] = bv * ke[kb][j] * (j < 4 ? wa[j] : wb[j - 4]);
+      }
+      store_ws8(static_cast<ws_t*>(a.qh) + off0 + (size_t)kb * 512, qx);
+      store_ws8(static_cast<ws_t*>(a.kh) + off0 + (size_t)kb * 512, kx);
+      store_ws4(sSK + i * SP + d0, wx);
+      store_ws4(sSK + i * SP + d0 + 16, wx + 4);
+    }
+  }
+  __syncthreads();   // sL and sSK complete; sKE and the tables are dead
+  GDR_PPROF(3);
+
+  if constexpr (DUMP) {
+    if (a.d_akk) dump_akk(a.d_akk + (size_t)cid * C * C, sL, tid);
+    if (a.d_aqk) dump_aqk(a.d_aqk + (size_t)cid * C * C, aqT, wave, r, grp);
+  }
+
+  // ---- M^-1, then the folded operands ------------------------------------------
+  unit_lower_inverse<P>(sL, sMT, tid, wave, r, grp);
+  GDR_PPROF(4);
+  if constexpr (DUMP) {
+    if (a.d_minv) dump_minv(a.d_minv + (size_t)cid * C * C, sMT, tid);
+  }
+  fold_w<K, P, false>(sMT, static_cast<ws_t*>(a.wt) + (size_t)cid * K * C, wave, lane, r, grp,
+                      [&](int c, int d) { return (float)sSK[c * SP + d]; },
+                      [&](int) { return 1.f; });
+  GDR_PPROF(5);
+  fold_aqk<P>(aqT, sMT, static_cast<ws_t*>(a.ah) + (size_t)cid * C * C, wave, lane, r, grp);
+  GDR_PPROF(6);
+}
+
+}  // namespace gdr

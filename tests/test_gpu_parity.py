@@ -167,6 +167,27 @@ def test_positive_g(gpu_lib, per_channel):
     check(o, s, *oracle_full(inp), "bf16", "positive g")
 
 
+@pytest.mark.parametrize("mu", [-1.0, -3.0])
+def test_per_channel_strong_decay(gpu_lib, mu):
+    """Per-channel g = logsigmoid(N(mu, 1)): decays of e^-1..e^-3 per token, so
+    one 16-row block spans e^-20..e^-50 in most channels (the diagonal tiles'
+    fp32 factorisation about the middle row)."""
+    inp = make_inputs(small(per_channel=True, T=200, mu=mu))
+    o, s = run_gpu(gpu_lib, inp)
+    check(o, s, *oracle_full(inp), "bf16", f"strong decay mu={mu}")
+
+
+def test_per_channel_mixed_extreme_decay(gpu_lib):
+    """A few channels forget within a token (g = -30: over half a block the
+    decay passes e^-80, the explicit diagonal path) next to slow channels."""
+    inp = make_inputs(small(per_channel=True, T=200, mu=4.0))
+    rng = np.random.default_rng(11)
+    fast = rng.random(inp.g.shape) < 0.05
+    inp.g[fast] = -30.0
+    o, s = run_gpu(gpu_lib, inp)
+    check(o, s, *oracle_full(inp), "bf16", "mixed extreme decay")
+
+
 def test_beta0_g0_keeps_state(gpu_lib):
     inp = make_inputs(small(T=150))
     inp.g[...] = 0.0
