@@ -30,6 +30,9 @@ def flags():
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU ops stay off (see the numerics notes in gdr.h)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: the state and the products
+            # are also touched by VALU code, which cannot read AGPRs directly
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 

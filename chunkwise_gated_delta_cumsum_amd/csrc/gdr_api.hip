@@ -93,7 +93,9 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
 size_t nchunks(const Prob& r) { return (size_t)r.B * r.HV * r.N; }
 
 WsLayout layout(const Prob& r) {
-  const size_t qk = r.perch ? nchunks(r) : (size_t)r.B * r.H * r.N;
+  // q/k fragments with the decay folded in exist only per channel; with one
+  // decay per row the scan reads q and k from the inputs
+  const size_t qk = r.perch ? nchunks(r) : 0;
   return ws_layout(nchunks(r), qk, r.K, r.V, r.es, (size_t)r.B * r.HV, r.nseg);
 }
 
@@ -203,7 +205,7 @@ gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
     st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain>,
                 grid_for(BH * (r.nseg - 1), (K + V) / kScanBV), kScanWaves * 64, a, s);
     if (st != GDR_OK) return st;
-    st = launch(seg_combine_kernel<K, V, P>, grid_for(BH, V / kScanBV), kScanWaves * 64, a, s);
+    st = launch(seg_combine_kernel<K, V, P>, grid_for(BH, V / kScanBV), kCombineWaves * 64, a, s);
     if (st != GDR_OK) return st;
   }
   return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull>,

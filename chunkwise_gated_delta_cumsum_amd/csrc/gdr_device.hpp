@@ -24,6 +24,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;
 
@@ -36,6 +37,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Index of this wave in its workgroup, as a scalar.  Branches on it are then
+// uniform scalar branches: an MFMA inside one is skipped as a whole instead of
+// running under a partial EXEC mask, which MFMA does not honour.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 
 // ---- products -------------------------------------------------------------
 // 16x16 tile += (16 x 32) * (32 x 16)
@@ -80,6 +88,20 @@ struct PolicyF16 {
     for (int i = 0; i < 8; ++i) f[i] = valid ? (_Float16)bf16_to_f32(x[i]) : (_Float16)0.f;
     return f;
   }
+  // exact for every bf16 value inside the fp16 range (8 < 11 mantissa bits),
+  // so the rounding mode of the packed conversion never matters there
+  __device__ static __forceinline__ frag_t frag_from_raw(raw_t x) {
+    const u32x4 d = __builtin_bit_cast(u32x4, x);
+    frag_t f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto h2 = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d[i] << 16),
+                                                 __uint_as_float(d[i] & 0xffff0000u));
+      f[2 * i] = h2[0];
+      f[2 * i + 1] = h2[1];
+    }
+    return f;
+  }
   __device__ static __forceinline__ float in_to_f32(in_t x) { return bf16_to_f32(x); }
   __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return bf16_to_f32(x[i]); }
   // 16x16 tile += (16 x 16) * (16 x 16), lane holds k = 4*grp + i; fp16
@@ -121,6 +143,7 @@ struct PolicyF32 {
     for (int i = 0; i < 8; ++i) f[i] = valid ? x[i] : 0.f;
     return f;
   }
+  __device__ static __forceinline__ frag_t frag_from_raw(raw_t x) { return x; }
   __device__ static __forceinline__ float in_to_f32(in_t x) { return x; }
   __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return x[i]; }
   __device__ static __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {
@@ -231,10 +254,9 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 //   ah : A^ = A_qk M^-1 as an A operand (rows i, k = c): [4][2][64][8]
 //   rs : 256 fp32: [0..63] exp(gamma_c) (one decay per row; 1 per channel),
 //        [64..64+K) exp(gamma_last) per key channel
-//   qh, kh : q and k as A operands (rows c, k = d): [4][K/32][64][8].  With
-//        one decay per row they are the raw inputs, stored once per (batch,
-//        q/k head, chunk); with per-channel decay they are q exp(gamma) scale
-//        and k exp(gamma), stored per value head.
+//   qh, kh : per-channel decay only: q exp(gamma) scale and k exp(gamma) as A
+//        operands (rows c, k = d): [4][K/32][64][8] per value-head chunk.
+//        With one decay per row the scan reads q and k from the inputs.
 //   seg, phi, eend : sequence segments (when more than one): start states
 //        [B*HV][nseg][K*V], transitions [B*HV][nseg-1][K][K] and zero-start end
 //        states [B*HV][nseg-1][K*V], fp32.
@@ -245,7 +267,7 @@ struct WsLayout {
 __host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // nchunks = B * HV * N value-head chunks; qkchunks = chunks that carry their
-// own q/k fragments (B * H * N with one decay per row, nchunks per channel).
+// own q/k fragments (0 with one decay per row, nchunks per channel).
 __host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, int K, int V,
                                               size_t elem, size_t nheads, int nseg) {
   WsLayout L;

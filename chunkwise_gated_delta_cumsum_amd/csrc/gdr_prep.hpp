@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   __shared__ float sKs[C];     // beta_c exp(gamma_last - gamma_c)
   float* sMT = reinterpret_cast<float*>(sQbuf);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = lane & 15, grp = lane >> 4;
   int b, hv, n;
   if (!prep_block(a.B, a.H, a.HV / a.H, a.N, b, hv, n)) return;
@@ -346,27 +346,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     }
   }
 
-  // q and k as A fragments for the scan (rows c, k = d): the raw inputs in
-  // the workspace type, written once per (batch, q/k head, chunk) by the
-  // first value head of the group.
-  if ((hv % (a.HV / a.H)) == 0) {
-    const size_t fid = ((size_t)b * a.H + h) * a.N + n;
-    for (int e = tid; e < 4 * KB * 64; e += 256) {
-      const int ln = e & 63, f = e >> 6, rt = f / KB, kb = f % KB;
-      const int c = 16 * rt + (ln & 15), gg = ln >> 4;
-      const auto qr = P::load_raw(sQ + c * KP + 32 * kb, gg);
-      const auto kr = P::load_raw(sK + c * KP + 32 * kb, gg);
-      float qx[8], kx[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        qx[s] = P::raw_f32(qr, s);
-        kx[s] = P::raw_f32(kr, s);
-      }
-      const size_t off = ((fid * 4 + rt) * KB + kb) * 512 + ln * 8;
-      store_ws8(static_cast<ws_t*>(a.qh) + off, qx);
-      store_ws8(static_cast<ws_t*>(a.kh) + off, kx);
-    }
-  }
   __syncthreads();   // sL complete
   GDR_PPROF(2);
 

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   float* sCf = sSf + 4 * K;                                      // [6][K] exp(pre[I] - pre[J+1])
   float* sMT = reinterpret_cast<float*>(sX);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = lane & 15, grp = lane >> 4;
   int b, hv, n;
   if (!prep_block(a.B, a.H, a.HV / a.H, a.N, b, hv, n)) return;

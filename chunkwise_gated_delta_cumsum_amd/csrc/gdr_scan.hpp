@@ -20,18 +20,26 @@
 //                 writing o, in parallel over segments.
 // With one segment only the full mode runs.
 //
-// Work split in a workgroup of 4 waves (64 state columns): wave w owns chunk
-// rows [16w, 16w+16) of Y, Z and o and state rows [K/4 w, K/4 (w+1)).  Every
-// A-operand fragment (q, k, W^T and A^ rows) belongs to exactly one wave,
-// which loads it from the workspace straight into registers one chunk ahead,
-// 16 bytes per lane and 1 KB per instruction, interleaved with the MFMAs so
-// the memory and matrix pipes run together.  Only the B operands S and Z are
-// shared, through LDS in fragment order (accumulator tiles are B fragments,
-// see gdr_device.hpp), with two barriers per chunk.  v arrives as 16-byte
-// row pieces and is turned into accumulator layout through a per-wave LDS
-// tile; o leaves the same way.  The fp32 state never leaves registers
-// except at segment ends.
+// Work split in a workgroup of two waves (64 state columns, a "slab"): wave w
+// owns chunk rows [32w, 32w+32) of Y, Z and o and state rows [K/2 w,
+// K/2 (w+1)).  Every A-operand fragment (k, q, W^T and A^ rows) belongs to
+// exactly one wave, which loads it straight into registers and reloads it for
+// the next chunk as soon as its products are issued.  Only the B operands
+// S and Z cross between the two waves, through LDS in fragment order
+// (accumulator tiles are B fragments, see gdr_device.hpp), with two barriers
+// per chunk.  The output is formed transposed, o^T = S^T q^T + Z^T A^T: the B
+// fragments of S and Z are also A fragments of S^T and Z^T, and the q and A^
+// fragments are B fragments of q^T and A^T, so no operand moves, and each
+// lane ends up with four consecutive columns of one o row (16-byte stores).
+// v arrives as 16-byte row pieces and reaches accumulator layout through a
+// per-wave LDS tile.  The fp32 state never leaves registers except at
+// segment ends.
+//
+// With one decay per row the k and q fragments come straight from the bf16
+// (or fp32) inputs; with per-channel decay they are the prep kernel's
+// k exp(gamma) and q exp(gamma) scale.
 #pragma once
+#include <type_traits>
 #include "gdr_device.hpp"
 
 namespace gdr {
@@ -70,8 +78,9 @@ __device__ long long gdr_scan_prof[64 * 8 * 4];
 
 constexpr int kScanFull = 0;
 constexpr int kScanChain = 1;
-constexpr int kScanBV = 64;   // state columns per workgroup
+constexpr int kScanBV = 64;     // state columns per workgroup
 constexpr int kScanWaves = 4;
+constexpr int kCombineWaves = 4;
 
 // Barrier for LDS traffic only: wait for this wave's LDS operations, then
 // the workgroup barrier.  Outstanding global loads (the next chunk's
@@ -104,118 +113,155 @@ __device__ __forceinline__ bool unit_block(int nunits, int nslab, int& unit, int
   return unit < nunits;
 }
 
-// Offset of the state tiles owned by (slab sv, wave w) inside one K x V state
-// stored in tile order: [slab][wave][SRT][NCT][64 lanes][4].
-template <int K, int V>
-__device__ __forceinline__ size_t tile_off(int sv, int w) {
-  return ((size_t)sv * kScanWaves + w) * (K / 64) * (kScanBV / 16) * 256;
+// Offset (floats) of accumulator tile (state row tile dt, column tile ct) of
+// slab sv inside one K x V state kept in tile order:
+// [slab][row tile][column tile][64 lanes][4].
+template <int K>
+__device__ __forceinline__ size_t state_tile(int sv, int dt, int ct) {
+  return (((size_t)sv * (K / 16) + dt) * (kScanBV / 16) + ct) * 256;
 }
 
-template <int K, int V, bool PERCH, class P, int MODE>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
+// One wave of a scan workgroup.  W (the wave index) and PHI (chain mode:
+// transition slab, identity start and no v) are template arguments so that
+// every choice between waves and slab kinds folds at compile time.
+template <int K, int V, bool PERCH, class P, int MODE, int NW, int W, bool PHI>
+__device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t* sS,
+                                          typename P::frag_t* sZ, typename P::in_t* sVw,
+                                          int unit, int sv) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
   using ws_t = typename P::ws_t;
+  using raw_t = typename P::raw_t;
+  // k / q operands as held between load and use: workspace fragments with
+  // per-channel decay, raw input elements otherwise
+  using kq_t = std::conditional_t<PERCH, frag_t, raw_t>;
   constexpr bool FULL = MODE == kScanFull;
   constexpr int C = kChunk;
   constexpr int BV = kScanBV;
-  constexpr int NSLAB = FULL ? V / BV : (K + V) / BV;   // chain: Phi slabs, then E slabs
   constexpr int NCT = BV / 16;     // column tiles
   constexpr int KT = K / 16;       // state row tiles
   constexpr int KB = K / 32;       // 32-wide k blocks over K
-  constexpr int SRT = KT / 4;      // state row tiles per wave
+  constexpr int SRT = KT / NW;     // state row tiles per wave
+  constexpr int CT = 4 / NW;       // chunk row tiles per wave
+  constexpr int CR = 16 * CT;      // chunk rows per wave
   constexpr int VVEC = 16 / (int)sizeof(in_t);       // v elements per 16 bytes
   constexpr int VPR = BV / VVEC;                     // 16-byte pieces per v row
   constexpr int VRI = 64 / VPR;                      // v rows per load instruction
-  constexpr int VNI = 16 / VRI;                      // load instructions per wave
+  constexpr int VNI = CR / VRI;                      // load instructions per wave
   constexpr int VP = BV + VVEC;                      // padded LDS v row
-  constexpr int OP = BV + 4;                         // padded LDS o row (fp32)
+  constexpr int w = W;
+  // k blocks of c (32 rows) that meet this wave's rows in A^ (lower triangular)
+  constexpr int AKB = (CR * (w + 1) + 31) / 32;
 
-  __shared__ frag_t sS[KB * NCT * 64];                // B fragments of S
-  __shared__ frag_t sZ[2 * NCT * 64];                 // B fragments of Z
-  __shared__ __attribute__((aligned(16))) in_t sV[kScanWaves][16 * VP];
-  __shared__ __attribute__((aligned(16))) float sO[FULL ? kScanWaves : 1][FULL ? 16 * OP : 4];
-
-  const int nsegu = FULL ? a.nseg : a.nseg - 1;       // segments handled by this pass
-  int unit, sv;
-  if (!unit_block(a.B * a.HV * nsegu, NSLAB, unit, sv)) return;
+  const int nsegu = FULL ? a.nseg : a.nseg - 1;
   const int bh = unit / nsegu, p = unit % nsegu;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15, grp = lane >> 4;
   const int b = bh / a.HV, hv = bh % a.HV;
   const int h = hv / (a.HV / a.H);
   const int T = a.T;
-  // chain mode: slabs [0, K/64) carry columns of the transition (identity
-  // start, no v), the rest the zero-start end state
-  const bool isphi = !FULL && sv < K / BV;
-  const int v0 = FULL ? sv * BV : (isphi ? 0 : (sv - K / BV) * BV);
+  // chain mode: slabs [0, K/64) carry columns of the transition, the rest the
+  // zero-start end state
+  const int v0 = FULL ? sv * BV : (PHI ? 0 : (sv - K / BV) * BV);
   const int n0 = p * a.seg_len;
   const int n1 = min(n0 + a.seg_len, a.N);
 
   const in_t* vg = static_cast<const in_t*>(a.v);
   const ws_t* wtg = static_cast<const ws_t*>(a.wt);
   const ws_t* ahg = static_cast<const ws_t*>(a.ah);
-  const ws_t* qhg = static_cast<const ws_t*>(a.qh);
-  const ws_t* khg = static_cast<const ws_t*>(a.kh);
 
-  float zf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const frag_t fzero = P::make(zf);
-
-  // Per-chunk operands of this wave, as loaded.
-  struct Ops {
-    frag_t kf[KB], qf[KB];
-    frag_t wf[SRT][2], af[2];
-    uint4 vr[VNI];
-    f32x4 eg;
-    f32x4 dl[SRT];
+  // ---- per-chunk operands of this wave, reloaded right after their use -----
+  // k, q and v are reloaded as soon as their last use is issued; the rest is
+  // double-buffered and loaded early in the previous chunk, so that no wait
+  // at the top of the chunk loop (where the compiler's accounting of loads in
+  // flight is conservative) finds a load issued late.
+  u32x4 vr[VNI];
+  struct WA {
+    kq_t kf[CT][KB], qf[CT][KB];
+    frag_t wf[SRT][2], af[CT][2];
+    f32x4 eg[CT];                        // exp(gamma), rows CR w + 16ct + 4grp + j
+    float ego[CT];                       // exp(gamma), row CR w + 16ct + r
+    f32x4 dl[PERCH ? SRT : 1];           // exp(gamma_last) per state row (one value
+                                         // for every row with scalar decay)
   };
-
-  // The operand loads of one chunk as a list of items; the chunk loop issues
-  // them one at a time between MFMAs so that the memory pipe and the matrix
-  // pipe stay busy together (a wave issues in order).
-  constexpr int IT_V = 0, IT_K = IT_V + VNI, IT_Q = IT_K + KB, IT_EG = IT_Q + KB;
-  constexpr int IT_W = IT_EG + 1, IT_A = IT_W + 2 * SRT, IT_DL = IT_A + 2;
-  constexpr int NITEMS = IT_DL + SRT;
-  auto load_item = [&](int i, int n, Ops& op) {
-    const size_t cid = (size_t)bh * a.N + n;
-    const size_t fid = PERCH ? cid : ((size_t)b * a.H + h) * a.N + n;
-    const int t0 = n * C;
-    const float* rs = a.rs + cid * 256;
-    if (i < IT_K) {
-      if (!isphi) {
-        // v rows; tail rows read a valid row and are zeroed in the LDS write
-        const int t = min(t0 + 16 * w + VRI * (i - IT_V) + lane / VPR, T - 1);
-        op.vr[i - IT_V] = *reinterpret_cast<const uint4*>(
-            vg + (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % VPR) * VVEC);
-      }
-    } else if (i < IT_Q) {
-      op.kf[i - IT_K] = frag_ws(khg + ((fid * 4 + w) * KB + (i - IT_K)) * 512 + lane * 8);
-    } else if (i < IT_EG) {
-      if constexpr (FULL)
-        op.qf[i - IT_Q] = frag_ws(qhg + ((fid * 4 + w) * KB + (i - IT_Q)) * 512 + lane * 8);
-    } else if (i < IT_W) {
-      op.eg = *reinterpret_cast<const f32x4*>(rs + 16 * w + 4 * grp);
-    } else if (i < IT_A) {
-      const int st = (i - IT_W) >> 1, kb = (i - IT_W) & 1;
-      op.wf[st][kb] = frag_ws(wtg + ((cid * KT + SRT * w + st) * 2 + kb) * 512 + lane * 8);
-    } else if (i < IT_DL) {
-      if constexpr (FULL) {
-        const int kb = i - IT_A;
-        op.af[kb] = (kb == 0 || w >= 2)
-                        ? frag_ws(ahg + ((cid * 4 + w) * 2 + kb) * 512 + lane * 8)
-                        : fzero;
-      }
+  auto kq_load = [&](const void* base, const ws_t* wsb, int n, int ct, int kb) -> kq_t {
+    if constexpr (PERCH) {
+      const size_t cid = (size_t)bh * a.N + n;
+      return frag_ws(wsb + ((cid * 4 + CT * w + ct) * KB + kb) * 512 + lane * 8);
     } else {
-      const int st = i - IT_DL;
-      op.dl[st] = *reinterpret_cast<const f32x4*>(rs + 64 + 16 * (SRT * w + st) + 4 * grp);
+      const int t = min(n * C + CR * w + 16 * ct + r, T - 1);
+      const in_t* row = static_cast<const in_t*>(base) + (((size_t)b * T + t) * a.H + h) * K;
+      return P::load_raw(row + 32 * kb, grp);
     }
   };
-  auto load = [&](int n, Ops& op) {
+  // Rows past T (read as row T-1) need no mask: their Z rows meet zero rows
+  // of W^ and zero columns of A^ (beta = 0 there), and their o is not stored.
+  auto kq_frag = [&](const kq_t& x) -> frag_t {
+    if constexpr (PERCH)
+      return x;
+    else
+      return P::frag_from_raw(x);
+  };
+  auto load_v = [&](int n) {
+    if constexpr (!PHI) {
 #pragma unroll
-    for (int i = 0; i < NITEMS; ++i) load_item(i, n, op);
+      for (int i = 0; i < VNI; ++i) {
+        // tail rows read row T-1 (see kq_frag)
+        const int t = min(n * C + CR * w + VRI * i + lane / VPR, T - 1);
+        vr[i] = *reinterpret_cast<const u32x4*>(
+            vg + (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % VPR) * VVEC);
+      }
+    }
+  };
+  // The next chunk's operands as a list of load items, issued one at a time
+  // between the products of the current chunk: a burst of them would stall
+  // the wave at issue (in order) while the memory pipeline drains it.
+  constexpr int IT_K = 0;
+  constexpr int IT_Q = IT_K + CT * KB;
+  constexpr int IT_W = IT_Q + (FULL ? CT * KB : 0);
+  constexpr int IT_A = IT_W + SRT * 2;
+  constexpr int IT_R = IT_A + (FULL ? CT * AKB : 0);
+  constexpr int NITEMS = IT_R + 1;
+  auto load_item = [&](int i, int n, WA& x) {
+    const size_t cid = (size_t)bh * a.N + n;
+    const float* rs = a.rs + cid * 256;
+    if (i < IT_Q) {
+      const int ct = (i - IT_K) / KB, kb = (i - IT_K) % KB;
+      x.kf[ct][kb] = kq_load(a.k, static_cast<const ws_t*>(a.kh), n, ct, kb);
+    } else if (i < IT_W) {
+      if constexpr (FULL) {
+        const int ct = (i - IT_Q) / KB, kb = (i - IT_Q) % KB;
+        x.qf[ct][kb] = kq_load(a.q, static_cast<const ws_t*>(a.qh), n, ct, kb);
+      }
+    } else if (i < IT_A) {
+      const int st = (i - IT_W) / 2, kb = (i - IT_W) % 2;
+      x.wf[st][kb] = frag_ws(wtg + ((cid * KT + SRT * w + st) * 2 + kb) * 512 + lane * 8);
+    } else if (i < IT_R) {
+      if constexpr (FULL) {
+        const int ct = (i - IT_A) / AKB, kb = (i - IT_A) % AKB;
+        x.af[ct][kb] = frag_ws(ahg + ((cid * 4 + CT * w + ct) * 2 + kb) * 512 + lane * 8);
+      }
+    } else {
+      if constexpr (PERCH) {
+#pragma unroll
+        for (int st = 0; st < SRT; ++st)
+          x.dl[st] = *reinterpret_cast<const f32x4*>(rs + 64 + 16 * (SRT * w + st) + 4 * grp);
+      } else {
+        x.dl[0][0] = rs[64];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          x.eg[ct] = *reinterpret_cast<const f32x4*>(rs + CR * w + 16 * ct + 4 * grp);
+          if constexpr (FULL) x.ego[ct] = rs[CR * w + 16 * ct + r];
+        }
+      }
+    }
+  };
+  auto load_wa = [&](int n, WA& x) {
+#pragma unroll
+    for (int i = 0; i < NITEMS; ++i) load_item(i, n, x);
   };
 
-  // state rows 16*(SRT*w + st) + 4*grp + j, columns v0 + 16*ct + r
+  // ---- state: rows 16(SRT w + st) + 4grp + j, columns v0 + 16ct + r ----------
   f32x4 S[SRT][NCT];
 #pragma unroll
   for (int st = 0; st < SRT; ++st)
@@ -223,12 +269,13 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
     for (int ct = 0; ct < NCT; ++ct) S[st][ct] = zero4();
   if constexpr (FULL) {
     if (p > 0) {
-      const float* src = a.seg_state + ((size_t)bh * a.nseg + p) * K * V + tile_off<K, V>(sv, w);
+      const float* src = a.seg_state + ((size_t)bh * a.nseg + p) * K * V;
 #pragma unroll
       for (int st = 0; st < SRT; ++st)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-          S[st][ct] = *reinterpret_cast<const f32x4*>(src + ((st * NCT + ct) * 64 + lane) * 4);
+          S[st][ct] = *reinterpret_cast<const f32x4*>(
+              src + state_tile<K>(sv, SRT * w + st, ct) + lane * 4);
     } else if (a.s0) {
 #pragma unroll
       for (int st = 0; st < SRT; ++st)
@@ -240,7 +287,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
             S[st][ct][j] = a.s0[((size_t)bh * K + d) * V + v0 + 16 * ct + r];
           }
     }
-  } else if (isphi) {
+  } else if constexpr (PHI) {
     // identity columns [64 sv, 64 sv + 64) of I_K
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
@@ -253,30 +300,43 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
         }
   }
 
-  in_t* sVw = sV[w];
-  float* sOw = sO[FULL ? w : 0];
+  load_v(n0);
 
-  // One chunk: consume `cur`, prefetch chunk n+1 into `nxt`.  The loop below
-  // alternates two operand sets, so the prefetch never waits for the loads
-  // it replaces.
-  auto body = [&](int n, const Ops& cur, Ops& nxt) {
-    GDR_PROF(0);
-    const int t0 = n * C;
+  // o^T of a chunk is stored at the top of the next iteration (or after the
+  // loop), after the wait for the loads in flight, so that wait never covers
+  // freshly issued stores
+  f32x4 OT[NCT][CT];
+  auto store_o = [&](int n) {
+    // lane holds o[row CR w + 16 c2 + r][columns v0 + 16ct + 4grp .. +3]
+#pragma unroll
+    for (int c2 = 0; c2 < CT; ++c2) {
+      const int t = n * C + CR * w + 16 * c2 + r;
+      if (t < T) {
+        float* orow = a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 + 4 * grp;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(orow + 16 * ct) = OT[ct][c2];
+      }
+    }
+  };
+
+  auto step = [&](int n, const WA& cur, WA& nxt) {
     const int nn = min(n + 1, n1 - 1);   // the last chunk reloads itself
-    int item = 0;
-    GDR_PROF(1);
-
-    // v rows of this wave into its LDS tile (zero past T)
-    if (!isphi) {
+    GDR_PROF(0);
+    // v rows of this wave into its LDS tile, the previous chunk's o, then the
+    // next chunk's v
+    if constexpr (!PHI) {
 #pragma unroll
       for (int i = 0; i < VNI; ++i) {
         const int row = VRI * i + lane / VPR;
-        const bool ok = t0 + 16 * w + row < T;
-        *reinterpret_cast<uint4*>(sVw + row * VP + (lane % VPR) * VVEC) =
-            ok ? cur.vr[i] : uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sVw + row * VP + (lane % VPR) * VVEC) = vr[i];
       }
     }
-    // publish this wave's state rows as halves of the S B-fragments
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FULL) {
+      if (n > n0) store_o(n - 1);
+    }
+    if constexpr (!PHI) load_v(nn);
+    // this wave's state rows as halves of the B fragments of S
 #pragma unroll
     for (int st = 0; st < SRT; ++st) {
       const int tile = SRT * w + st;
@@ -285,106 +345,127 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
         store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
     }
     lds_barrier();
-    GDR_PROF(2);
-
-    // Y = k S (and O = q S) for chunk rows [16w, 16w+16)
-    frag_t bS[KB][NCT];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) bS[kb][ct] = sS[(kb * NCT + ct) * 64 + lane];
-    f32x4 Y[NCT], O[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) { Y[ct] = zero4(); O[ct] = zero4(); }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        Y[ct] = mma32(cur.kf[kb], bS[kb][ct], Y[ct]);
-        if constexpr (FULL) O[ct] = mma32(cur.qf[kb], bS[kb][ct], O[ct]);
-        if (item < NITEMS) load_item(item++, nn, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    GDR_PROF(3);
-
-    // Z = v - exp(gamma) Y, published as halves of the Z B-fragments
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 z;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float vv = isphi ? 0.f : P::in_to_f32(sVw[(4 * grp + j) * VP + 16 * ct + r]);
-        if constexpr (PERCH) {
-          z[j] = vv - Y[ct][j];
-        } else {
-          z[j] = vv - cur.eg[j] * Y[ct][j];
-          if constexpr (FULL) O[ct][j] *= cur.eg[j] * a.scale;
-        }
-      }
-      store_half(&sZ[((w >> 1) * NCT + ct) * 64 + lane], w & 1, z);
-    }
-    GDR_PROF(4);
-    lds_barrier();
-    GDR_PROF(5);
-
-    frag_t zb[2][NCT];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) zb[kb][ct] = sZ[(kb * NCT + ct) * 64 + lane];
-
-    // S <- diag(exp(gamma_last)) S + W^T Z
-#pragma unroll
-    for (int st = 0; st < SRT; ++st)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[st][ct][j] *= cur.dl[st][j];
-        S[st][ct] = mma32(cur.wf[st][0], zb[0][ct], S[st][ct]);
-        S[st][ct] = mma32(cur.wf[st][1], zb[1][ct], S[st][ct]);
-        if (item < NITEMS) load_item(item++, nn, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-    for (; item < NITEMS; ++item) load_item(item, nn, nxt);
+    GDR_PROF(1);
+    int item = 0;
     GDR_PROF(6);
 
-    if constexpr (FULL) {
-      // o = O + A^ Z
+    // Y = k S and o^T = S^T q^T for chunk rows [CR w, CR (w+1)): each B fragment
+    // of S serves both (it is also the A fragment of S^T)
+    f32x4 Y[CT][NCT];
+#pragma unroll
+    for (int c2 = 0; c2 < CT; ++c2)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        O[ct] = mma32(cur.af[0], zb[0][ct], O[ct]);
-        if (w >= 2) O[ct] = mma32(cur.af[1], zb[1][ct], O[ct]);
+        Y[c2][ct] = zero4();
+        OT[ct][c2] = zero4();
       }
-      // o rows through this wave's LDS tile, then 16-byte row stores
+    {
+      // every B fragment of S at once, so the LDS latency is paid once
+      frag_t bS[KB][NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sOw[(4 * grp + j) * OP + 16 * ct + r] = O[ct][j];
-      constexpr int OPR = BV / 4;          // 16-byte pieces per o row
-      constexpr int ORI = 64 / OPR;        // rows per store instruction
+        for (int ct = 0; ct < NCT; ++ct) bS[kb][ct] = sS[(kb * NCT + ct) * 64 + lane];
+      GDR_PROF(7);
 #pragma unroll
-      for (int i = 0; i < 16 / ORI; ++i) {
-        const int row = ORI * i + lane / OPR, c4 = (lane % OPR) * 4;
-        const int t = t0 + 16 * w + row;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(sOw + row * OP + c4);
-        if (t < T)
-          *reinterpret_cast<f32x4*>(a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 + c4) = x;
+      for (int kb = 0; kb < KB; ++kb) {
+        frag_t fk[CT], fq[CT];
+#pragma unroll
+        for (int c2 = 0; c2 < CT; ++c2) {
+          fk[c2] = kq_frag(cur.kf[c2][kb]);
+          if constexpr (FULL) fq[c2] = kq_frag(cur.qf[c2][kb]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int c2 = 0; c2 < CT; ++c2) {
+            Y[c2][ct] = mma32(fk[c2], bS[kb][ct], Y[c2][ct]);
+            if constexpr (FULL) OT[ct][c2] = mma32(bS[kb][ct], fq[c2], OT[ct][c2]);
+          }
+          if (item < NITEMS) load_item(item++, nn, nxt);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    GDR_PROF(7);
+    GDR_PROF(2);
+
+    // Z = v - exp(gamma) Y, published as halves of the B fragments of Z
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 z[CT];
+#pragma unroll
+      for (int c2 = 0; c2 < CT; ++c2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float vv =
+              PHI ? 0.f : P::in_to_f32(sVw[(16 * c2 + 4 * grp + j) * VP + 16 * ct + r]);
+          if constexpr (PERCH)
+            z[c2][j] = vv - Y[c2][ct][j];
+          else
+            z[c2][j] = vv - cur.eg[c2][j] * Y[c2][ct][j];
+        }
+#pragma unroll
+      for (int c2 = 0; c2 < CT; ++c2) {
+        const int tile = CT * w + c2;
+        store_half(&sZ[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, z[c2]);
+      }
+    }
+    lds_barrier();
+    GDR_PROF(3);
+
+    // S <- diag(exp(gamma_last)) S + W^T Z, and o^T = exp(gamma) scale o^T + Z^T A^T
+    float sc[CT];
+#pragma unroll
+    for (int c2 = 0; c2 < CT; ++c2) sc[c2] = (FULL && !PERCH) ? cur.ego[c2] * a.scale : 1.f;
+    frag_t bZ[2][NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      bZ[0][ct] = sZ[(0 * NCT + ct) * 64 + lane];
+      bZ[1][ct] = sZ[(1 * NCT + ct) * 64 + lane];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const frag_t z0 = bZ[0][ct];
+      const frag_t z1 = bZ[1][ct];
+#pragma unroll
+      for (int st = 0; st < SRT; ++st) {
+        if constexpr (PERCH)
+          S[st][ct] *= cur.dl[st];
+        else
+          S[st][ct] *= cur.dl[0][0];
+        S[st][ct] = mma32(cur.wf[st][0], z0, S[st][ct]);
+        S[st][ct] = mma32(cur.wf[st][1], z1, S[st][ct]);
+        if (item < NITEMS) load_item(item++, nn, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (FULL) {
+#pragma unroll
+        for (int c2 = 0; c2 < CT; ++c2) {
+          if constexpr (!PERCH) OT[ct][c2] *= sc[c2];
+          OT[ct][c2] = mma32(z0, cur.af[c2][0], OT[ct][c2]);
+          if constexpr (AKB > 1) OT[ct][c2] = mma32(z1, cur.af[c2][1], OT[ct][c2]);
+        }
+      }
+    }
+#pragma unroll
+    for (; item < NITEMS; ++item) load_item(item, nn, nxt);
+    GDR_PROF(4);
+
+    GDR_PROF(5);
   };
 
-  Ops bufA, bufB;
-  load(n0, bufA);
+  // two chunks per iteration with the operand buffers in swapped roles
+  WA bufA, bufB;
   int n = n0;
+  load_wa(n0, bufA);
   for (; n + 1 < n1; n += 2) {
-    body(n, bufA, bufB);
-    body(n + 1, bufB, bufA);
+    step(n, bufA, bufB);
+    step(n + 1, bufB, bufA);
   }
-  if (n < n1) body(n, bufA, bufB);
+  if (n < n1) step(n, bufA, bufB);
 
   if constexpr (FULL) {
+    store_o(n1 - 1);
     if (a.sT && p == a.nseg - 1) {
 #pragma unroll
       for (int st = 0; st < SRT; ++st)
@@ -396,7 +477,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
             a.sT[((size_t)bh * K + d) * V + v0 + 16 * ct + r] = S[st][ct][j];
           }
     }
-  } else if (isphi) {
+  } else if constexpr (PHI) {
     // Phi columns [64 sv, 64 sv + 64), row-major
     float* dst = a.phi + ((size_t)bh * (a.nseg - 1) + p) * K * K;
 #pragma unroll
@@ -409,19 +490,55 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(ScanArgs a) {
           dst[(size_t)d * K + sv * BV + 16 * ct + r] = S[st][ct][j];
         }
   } else {
-    float* dst = a.eend + ((size_t)bh * (a.nseg - 1) + p) * K * V +
-                 tile_off<K, V>(sv - K / BV, w);
+    float* dst = a.eend + ((size_t)bh * (a.nseg - 1) + p) * K * V;
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        *reinterpret_cast<f32x4*>(dst + ((st * NCT + ct) * 64 + lane) * 4) = S[st][ct];
+        *reinterpret_cast<f32x4*>(dst + state_tile<K>(sv - K / BV, SRT * w + st, ct) +
+                                  lane * 4) = S[st][ct];
   }
 }
 
+template <int K, int V, bool PERCH, class P, int MODE>
+__global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a) {
+  using in_t = typename P::in_t;
+  using frag_t = typename P::frag_t;
+  constexpr int NW = kScanWaves;
+  constexpr bool FULL = MODE == kScanFull;
+  constexpr int NSLAB = FULL ? V / kScanBV : (K + V) / kScanBV;
+  constexpr int NCT = kScanBV / 16;
+  constexpr int KB = K / 32;
+  constexpr int VVEC = 16 / (int)sizeof(in_t);
+  constexpr int VP = kScanBV + VVEC;
+  __shared__ frag_t sS[KB * NCT * 64];                // B fragments of S
+  __shared__ frag_t sZ[2 * NCT * 64];                 // B fragments of Z
+  __shared__ __attribute__((aligned(16))) in_t sV[NW][(64 / NW) * VP];
+
+  const int nsegu = FULL ? a.nseg : a.nseg - 1;       // segments handled by this pass
+  int unit, sv;
+  if (!unit_block(a.B * a.HV * nsegu, NSLAB, unit, sv)) return;
+  const int wv = wave_id();
+  auto run = [&](auto phi) {
+    constexpr bool PHI = decltype(phi)::value;
+    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, NW, 0, PHI>(a, sS, sZ, sV[0], unit, sv);
+    if constexpr (NW > 1)
+      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, NW, 1, PHI>(a, sS, sZ, sV[1], unit, sv);
+    if constexpr (NW > 2) {
+      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, NW, 2, PHI>(a, sS, sZ, sV[2], unit, sv);
+      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, NW, 3, PHI>(a, sS, sZ, sV[3], unit, sv);
+    }
+  };
+  if (FULL || sv >= K / kScanBV)
+    run(std::false_type{});
+  else if constexpr (!FULL)
+    run(std::true_type{});
+}
+
 // Combine pass: S_{p+1} = Phi_p S_p + E_p over the segments of one head,
-// one workgroup per (head, 64-column slab), same tile ownership as the scan.
-// Writes the start state of every segment p >= 1 in tile order.
+// one workgroup of four waves per (head, 64-column slab); wave w owns state
+// rows [K/4 w, K/4 (w+1)).  Phi_{p+1} and E_{p+1} are loaded while step p
+// computes.  Writes the start state of every segment p >= 1 in tile order.
 template <int K, int V, class P>
 __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
   using frag_t = typename P::frag_t;
@@ -430,15 +547,39 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
   constexpr int NCT = BV / 16;
   constexpr int KT = K / 16;
   constexpr int KB = K / 32;
-  constexpr int SRT = KT / 4;
+  constexpr int SRT = KT / kCombineWaves;
 
   __shared__ frag_t sS[KB * NCT * 64];
 
   int bh, sv;
   if (!unit_block(a.B * a.HV, NSLAB, bh, sv)) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int r = lane & 15, grp = lane >> 4;
   const int v0 = sv * BV;
+  const int nstep = a.nseg - 1;
+
+  struct Ops {
+    f32x4 ph[SRT][KB][2];   // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
+    f32x4 e[SRT][NCT];
+  };
+  auto load = [&](int p, Ops& op) {
+    const float* ph = a.phi + ((size_t)bh * nstep + p) * K * K;
+    const float* e = a.eend + ((size_t)bh * nstep + p) * K * V;
+#pragma unroll
+    for (int st = 0; st < SRT; ++st) {
+      const int d = 16 * (SRT * w + st) + r;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        op.ph[st][kb][0] = *reinterpret_cast<const f32x4*>(ph + (size_t)d * K + 32 * kb + 4 * grp);
+        op.ph[st][kb][1] =
+            *reinterpret_cast<const f32x4*>(ph + (size_t)d * K + 32 * kb + 16 + 4 * grp);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        op.e[st][ct] = *reinterpret_cast<const f32x4*>(
+            e + state_tile<K>(sv, SRT * w + st, ct) + lane * 4);
+    }
+  };
 
   f32x4 S[SRT][NCT];
 #pragma unroll
@@ -457,7 +598,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
         }
   }
 
-  for (int p = 0; p + 1 < a.nseg; ++p) {
+  auto step = [&](int p, const Ops& cur) {
 #pragma unroll
     for (int st = 0; st < SRT; ++st) {
       const int tile = SRT * w + st;
@@ -466,35 +607,39 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
         store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
     }
     lds_barrier();
-    const float* ph = a.phi + ((size_t)bh * (a.nseg - 1) + p) * K * K;
-    const float* e = a.eend + ((size_t)bh * (a.nseg - 1) + p) * K * V + tile_off<K, V>(sv, w);
-    f32x4 acc[SRT][NCT];
+#pragma unroll
+    for (int st = 0; st < SRT; ++st)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) S[st][ct] = cur.e[st][ct];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const frag_t fb = sS[(kb * NCT + ct) * 64 + lane];
+#pragma unroll
+        for (int st = 0; st < SRT; ++st)
+          S[st][ct] = mma32(P::make2(cur.ph[st][kb][0], cur.ph[st][kb][1]), fb, S[st][ct]);
+      }
+    float* dst = a.seg_state + ((size_t)bh * a.nseg + p + 1) * K * V;
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        acc[st][ct] = *reinterpret_cast<const f32x4*>(e + ((st * NCT + ct) * 64 + lane) * 4);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int st = 0; st < SRT; ++st) {
-        const int d = 16 * (SRT * w + st) + r;
-        const frag_t fa = frag_row_f32<P>(ph + (size_t)d * K + 32 * kb, grp);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          acc[st][ct] = mma32(fa, sS[(kb * NCT + ct) * 64 + lane], acc[st][ct]);
-      }
-    }
-    float* dst = a.seg_state + ((size_t)bh * a.nseg + p + 1) * K * V + tile_off<K, V>(sv, w);
-#pragma unroll
-    for (int st = 0; st < SRT; ++st)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        S[st][ct] = acc[st][ct];
-        *reinterpret_cast<f32x4*>(dst + ((st * NCT + ct) * 64 + lane) * 4) = acc[st][ct];
-      }
+        *reinterpret_cast<f32x4*>(dst + state_tile<K>(sv, SRT * w + st, ct) + lane * 4) =
+            S[st][ct];
     lds_barrier();   // every wave has read sS before it is rewritten
+  };
+
+  Ops bufA, bufB;
+  load(0, bufA);
+  int p = 0;
+  for (; p + 1 < nstep; p += 2) {
+    load(p + 1, bufB);
+    step(p, bufA);
+    if (p + 2 < nstep) load(p + 2, bufA);
+    step(p + 1, bufB);
   }
+  if (p < nstep) step(p, bufA);
 }
 
 }  // namespace gdr
