@@ -32,6 +32,19 @@ __device__ __forceinline__ int kslot(int grp, int i) {
   return 4 * grp + (i & 3) + 16 * (i >> 2);
 }
 
+// Key-channel order of the state.  Products over key channels do not care
+// which channel sits in which k slot, so the state keeps its rows in an order
+// where fragment slot i of lane group g (state row kslot(g, i) of a 32-row
+// block) holds key channel 8g + i: every k or q fragment is then 8
+// consecutive channels of one input row, a single 16-byte load.  Row x of
+// the state is key channel chan_of_row(x); the inverse is row_of_chan.
+__host__ __device__ __forceinline__ int chan_of_row(int x) {
+  return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x & 31) >> 4) + (x & 3);
+}
+__host__ __device__ __forceinline__ int row_of_chan(int c) {
+  return (c & ~31) + 4 * ((c & 31) >> 3) + 16 * ((c & 7) >> 2) + (c & 3);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
@@ -80,6 +93,10 @@ struct PolicyF16 {
     const u16x4 lo = *reinterpret_cast<const u16x4*>(row + 4 * grp);
     const u16x4 hi = *reinterpret_cast<const u16x4*>(row + 16 + 4 * grp);
     return raw_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  // 8 consecutive input elements (16 bytes), in slot order
+  __device__ static __forceinline__ raw_t load_raw8(const in_t* p) {
+    return *reinterpret_cast<const raw_t*>(p);
   }
   // convert raw input elements to a fragment; zero when !valid
   __device__ static __forceinline__ frag_t from_raw(raw_t x, bool valid) {
@@ -135,6 +152,11 @@ struct PolicyF32 {
   __device__ static __forceinline__ raw_t load_raw(const in_t* row, int grp) {
     const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);
     const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 + 4 * grp);
+    return raw_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static __forceinline__ raw_t load_raw8(const in_t* p) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
     return raw_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ static __forceinline__ frag_t from_raw(raw_t x, bool valid) {

@@ -129,6 +129,7 @@ __device__ __forceinline__ void unit_lower_inverse(float* sL, float* sMT, int ti
 }
 
 // ---- step 4a: W^ = M^-T diag(s) k -> A fragments of W^T --------------------
+// W^T tile row x is key channel chan_of_row(x), the state's row order.
 // kval(c, d) returns the B element diag(s) k at row c, channel d when
 // kRowScale is false; with kRowScale, kval returns raw k and rscale(c) = s_c
 // multiplies the M^-T entries instead.
@@ -139,7 +140,7 @@ __device__ __forceinline__ void fold_w(const float* sMT, typename P::ws_t* wt_ch
   using ws_t = typename P::ws_t;
   for (int jd = wave; jd < K / 16; jd += 4) {
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    const int d = 16 * jd + r;
+    const int d = chan_of_row(16 * jd + r);   // W^T rows follow the state's row order
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float vb[8];

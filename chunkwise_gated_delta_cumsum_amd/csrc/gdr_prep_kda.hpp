@@ -6,8 +6,9 @@
 // every factor kept in range.
 //
 // Wave I owns the rows of block I (rows 16I..16I+15); lane (r, grp) holds row
-// 16I + r at the channels kslot(grp, .) of every 32-channel group, in
-// registers, from the global loads on.  Per chunk:
+// 16I + r at channels 8grp .. 8grp+7 of every 32-channel group (fragment
+// slot i holds channel 8grp + i: the state's key-channel order, see
+// chan_of_row), in registers, from the global loads on.  Per chunk:
 //   1. s = in-block inclusive cumsum of g (a DPP scan across the 16 lanes of
 //      a row), block totals to LDS; gamma_i = pre[I] + s_i with pre[m] the
 //      sum of the totals of the blocks before m.
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   const bool valid = t < T;
   GDR_PPROF(0);
 
-  // ---- loads: this lane's row, channels 32kb + kslot(grp, .) ---------------
+  // ---- loads: this lane's row, channels 32kb + 8grp + (0..7) ---------------
   raw_t qr[KB], kr[KB];
   f32x4 glo[KB], ghi[KB];
   float bv;
@@ -105,10 +106,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
     const float* grow = a.g + (((size_t)b * T + tt) * a.HV + hv) * K;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      qr[kb] = P::load_raw(qrow + 32 * kb, grp);
-      kr[kb] = P::load_raw(krow + 32 * kb, grp);
-      glo[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 4 * grp);
-      ghi[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 16 + 4 * grp);
+      qr[kb] = P::load_raw8(qrow + 32 * kb + 8 * grp);
+      kr[kb] = P::load_raw8(krow + 32 * kb + 8 * grp);
+      glo[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 8 * grp);
+      ghi[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 8 * grp + 4);
     }
     bv = a.beta[((size_t)b * T + tt) * a.HV + hv];
   }
@@ -127,8 +128,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
     float* dst = (r == 15 ? sTot : sMid) + I * K;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      *reinterpret_cast<f32x4*>(dst + 32 * kb + 4 * grp) = f32x4{s[kb][0], s[kb][1], s[kb][2], s[kb][3]};
-      *reinterpret_cast<f32x4*>(dst + 32 * kb + 16 + 4 * grp) = f32x4{s[kb][4], s[kb][5], s[kb][6], s[kb][7]};
+      *reinterpret_cast<f32x4*>(dst + 32 * kb + 8 * grp) = f32x4{s[kb][0], s[kb][1], s[kb][2], s[kb][3]};
+      *reinterpret_cast<f32x4*>(dst + 32 * kb + 8 * grp + 4) = f32x4{s[kb][4], s[kb][5], s[kb][6], s[kb][7]};
     }
   }
   if (grp == 0) sBeta[i] = bv;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
         const int p = it - 8, I2 = p < 1 ? 1 : (p < 3 ? 2 : 3), J2 = p - I2 * (I2 - 1) / 2;
         sCf[p * K + d] = __expf(pre[I2] - pre[J2 + 1]);
       } else {
-        rs[64 + d] = __expf(pre[4]);
+        rs[64 + row_of_chan(d)] = __expf(pre[4]);   // in the state's row order
       }
     }
     if (tid < C) rs[tid] = 1.f;
@@ -166,10 +167,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   bool far = false;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const f32x4 t15a = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 4 * grp);
-    const f32x4 t15b = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 16 + 4 * grp);
-    const f32x4 tma = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 4 * grp);
-    const f32x4 tmb = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 16 + 4 * grp);
+    const f32x4 t15a = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 8 * grp);
+    const f32x4 t15b = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 8 * grp + 4);
+    const f32x4 tma = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 8 * grp);
+    const f32x4 tmb = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 8 * grp + 4);
     float a1[8], b1[8], b2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int d = 32 * kb + kslot(grp, j);
+          const int d = 32 * kb + 8 * grp + j;
           float pre = 0.f;
           for (int m = 0; m < I; ++m) pre += sTot[m * K + d];
           dg[d] = pre + s[kb][j];
@@ -270,8 +271,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const frag_t fe = sKE[(J * KB + kb) * 64 + lane];
-        const f32x4 ca = *reinterpret_cast<const f32x4*>(cf + 32 * kb + 4 * grp);
-        const f32x4 cb = *reinterpret_cast<const f32x4*>(cf + 32 * kb + 16 + 4 * grp);
+        const f32x4 ca = *reinterpret_cast<const f32x4*>(cf + 32 * kb + 8 * grp);
+        const f32x4 cb = *reinterpret_cast<const f32x4*>(cf + 32 * kb + 8 * grp + 4);
         float fv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) fv[j] = (float)fe[j] * (j < 4 ? ca[j] : cb[j - 4]);
@@ -301,11 +302,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
     const size_t off0 = (size_t)cid * 4 * KB * 512 + ((size_t)I * KB) * 512 + lane * 8;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int d0 = 32 * kb + 4 * grp;
+      const int d0 = 32 * kb + 8 * grp;
       const f32x4 pa = *reinterpret_cast<const f32x4*>(sPf + I * K + d0);
-      const f32x4 pb = *reinterpret_cast<const f32x4*>(sPf + I * K + d0 + 16);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(sPf + I * K + d0 + 4);
       const f32x4 wa = *reinterpret_cast<const f32x4*>(sSf + I * K + d0);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(sSf + I * K + d0 + 16);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(sSf + I * K + d0 + 4);
       float qx[8], kx[8], wx[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       store_ws8(static_cast<ws_t*>(a.qh) + off0 + (size_t)kb * 512, qx);
       store_ws8(static_cast<ws_t*>(a.kh) + off0 + (size_t)kb * 512, kx);
       store_ws4(sSK + i * SP + d0, wx);
-      store_ws4(sSK + i * SP + d0 + 16, wx + 4);
+      store_ws4(sSK + i * SP + d0 + 4, wx + 4);
     }
   }
   __syncthreads();   // sL and sSK complete; sKE and the tables are dead

@@ -191,7 +191,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     } else {
       const int t = min(n * C + CR * w + 16 * ct + r, T - 1);
       const in_t* row = static_cast<const in_t*>(base) + (((size_t)b * T + t) * a.H + h) * K;
-      return P::load_raw(row + 32 * kb, grp);
+      return P::load_raw8(row + 32 * kb + 8 * grp);
     }
   };
   // Rows past T (read as row T-1) need no mask: their Z rows meet zero rows
@@ -284,7 +284,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int d = 16 * (SRT * w + st) + 4 * grp + j;
-            S[st][ct][j] = a.s0[((size_t)bh * K + d) * V + v0 + 16 * ct + r];
+            S[st][ct][j] = a.s0[((size_t)bh * K + chan_of_row(d)) * V + v0 + 16 * ct + r];
           }
     }
   } else if constexpr (PHI) {
@@ -474,7 +474,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int d = 16 * (SRT * w + st) + 4 * grp + j;
-            a.sT[((size_t)bh * K + d) * V + v0 + 16 * ct + r] = S[st][ct][j];
+            a.sT[((size_t)bh * K + chan_of_row(d)) * V + v0 + 16 * ct + r] = S[st][ct][j];
           }
     }
   } else if constexpr (PHI) {
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 16 * (SRT * w + st) + 4 * grp + j;
-          S[st][ct][j] = a.s0[((size_t)bh * K + d) * V + v0 + 16 * ct + r];
+          S[st][ct][j] = a.s0[((size_t)bh * K + chan_of_row(d)) * V + v0 + 16 * ct + r];
         }
   }
 
