@@ -18,6 +18,7 @@ intra-chunk matrix memory the scalar-g kernel page estimates.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -62,6 +63,39 @@ def algorithmic_flops(w):
     mac = (((C - 1) / 2 * K + (C + 1) / 2 * K) / G + (C - 1) / 2 * (K + V) + 3 * K * V
            + (C + 1) / 2 * V)
     return 2.0 * mac * w.B * w.T * w.HV
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "chunkwise_gated_delta_cumsum_amd", "csrc")
+
+
+def kernel_sources_sha256():
+    """Hash of the HIP sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(w, stage_kernels):
+    """HBM bytes per launch of a stage from the stored rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counts (already scaled by the plain-copy calibration), or None
+    when there are none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"counters_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    total = 0.0
+    found = False
+    for name, v in rec["kernels"].items():
+        if any(s in name for s in stage_kernels):
+            total += v["fetch_bytes"] + v["write_bytes"]
+            found = True
+    return total if found else None
 
 
 def cpu_baseline(inp, budget_s):
@@ -189,8 +223,29 @@ def main():
         step(sets[i % nsets], *evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
-    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    step_prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    step_scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+
+    # Per-stage launch durations: each stage alone, launched back to back over
+    # the rotating sets between one pair of events on the launch stream (the
+    # per-step events above also count the launch gaps inside a step).
+    def stage_ms(fn):
+        KI = max(K, 20)
+        for i in range(3):
+            fn(sets[i % nsets])
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for i in range(KI):
+            fn(sets[i % nsets])
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / KI
+
+    prep_ms = stage_ms(lambda d: gdr.gdr_chunk_prep(d["q"], d["k"], d["g"], d["beta"], chunk=w.chunk,
+                                                   scale=inp.scale, V=w.V, workspace=d["ws"]))
+    scan_ms = stage_ms(lambda d: gdr.gdr_chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                   d["ws"], d["s0"], chunk=w.chunk, scale=inp.scale,
+                                                   out=(d["o"], d["sT"])))
 
     # the path check: one more pass through the single-call entry point
     d = sets[0]
@@ -201,10 +256,15 @@ def main():
     same = bool(torch.equal(o_ref, d["o"]))
 
     tm = traffic_model(w)
-    kern = {"chunk_prep_kernel": (prep_ms, tm["prep"]), "chunk_scan_kernel": (scan_ms, tm["scan"])}
-    dom = max(kern, key=lambda k_: kern[k_][0])
-    dom_ms, dom_bytes = kern[dom]
+    # the two stages of the path; the scan stage is up to three kernels (chain
+    # pass, segment combine, full pass) launched by one gdr_chunk_scan call
+    stages = {"chunk_prep": (prep_ms, tm["prep"], ("chunk_prep",)),
+              "state_scan": (scan_ms, tm["scan"], ("chunk_scan_kernel", "seg_combine_kernel"))}
+    dom = max(stages, key=lambda k_: stages[k_][0])
+    dom_ms, dom_bytes, dom_kernels = stages[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w, dom_kernels)
+    nseg = gdr.scan_segments(prob)
     ms_per_step = elapsed / K * 1e3
     tokens = w.B * w.T
     flops = algorithmic_flops(w)
@@ -229,8 +289,11 @@ def main():
                    "inputs": w.dtype, "initial_state": w.s0_std > 0,
                    "accumulate": "fp32", "rotating_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
-                     "kernel_ms": {"chunk_prep_kernel": prep_ms, "chunk_scan_kernel": scan_ms},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
+                     "kernels": list(dom_kernels), "algorithmic_bytes": dom_bytes,
+                     "kernel_ms": {"chunk_prep": prep_ms, "state_scan": scan_ms},
+                     "step_stage_ms": {"chunk_prep": step_prep_ms, "state_scan": step_scan_ms},
+                     "scan_segments": nseg,
                      "path_compulsory_bytes": tm["compulsory"],
                      "path_hbm_frac": tm["compulsory"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak},

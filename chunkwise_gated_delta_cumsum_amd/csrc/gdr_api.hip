@@ -29,14 +29,20 @@ struct Prob {
 
 // Number of sequence segments for the state scan.  One segment runs the
 // serial scan over all N chunks with B*HV*V/64 workgroups.  P segments run a
-// chain pass (B*HV*(P-1)*(K+V)/64 workgroups, seg_len chunks each, about 0.6
-// of a full chunk step), a serial combine (P-1 steps, about 0.5 each) and the
-// full pass (B*HV*P*V/64 workgroups, seg_len chunks).  Workgroups beyond the
-// 256 compute units of an MI355X run in further rounds.  The estimate uses
-// problem sizes only, so the workspace size query needs no device query.
+// chain pass (B*HV*(P-1)*(K+V)/64 workgroups of seg_len chunks, each chunk
+// step about 0.7 of a full-pass step), a serial combine (P-1 steps of about
+// 1.7 full-pass steps each) and the full pass (B*HV*P*V/64 workgroups of
+// seg_len chunks).  A pass with up to 256 workgroups (one per compute unit
+// of an MI355X) takes seg_len steps; beyond that two workgroups share a
+// compute unit at about 1.6x the step time, in rounds of 512.  The constants
+// are fitted to measured scan times of the 4096-, 8192-, 16000- and
+// 65536-token workloads over forced segment counts.  The estimate uses problem
+// sizes only, so the workspace size query needs no device query.
 int choose_segments(int BH, int N, int K, int V, int& seg_len) {
-  // chain workgroups fit two per compute unit, full ones one
-  constexpr double kCU = 256.0, kChainSlots = 512.0, kChain = 0.6, kComb = 0.5, kLaunch = 2.0;
+  constexpr double kCU = 256.0, kShare = 1.6, kChain = 0.7, kComb = 1.7;
+  auto pass = [&](double wgs, double steps) {
+    return wgs <= kCU ? steps : steps * kShare * std::ceil(wgs / (2.0 * kCU));
+  };
   double best = 1e300;
   int bestP = 1;
   seg_len = N;
@@ -44,12 +50,8 @@ int choose_segments(int BH, int N, int K, int V, int& seg_len) {
     const int L = (N + P - 1) / P;
     const int Pe = (N + L - 1) / L;
     if (Pe != P) continue;
-    const double r3 = std::ceil((double)BH * P * (V / 64) / kCU);
-    double t = r3 * L;
-    if (P > 1) {
-      const double r1 = std::ceil((double)BH * (P - 1) * ((K + V) / 64) / kChainSlots);
-      t += r1 * L * kChain + (P - 1) * kComb + 2 * kLaunch;
-    }
+    double t = pass((double)BH * P * (V / 64), L);
+    if (P > 1) t += pass((double)BH * (P - 1) * ((K + V) / 64), L) * kChain + (P - 1) * kComb;
     if (t < best * 0.999) {
       best = t;
       bestP = P;

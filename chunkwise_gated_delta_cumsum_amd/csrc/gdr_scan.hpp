@@ -20,20 +20,23 @@
 //                 writing o, in parallel over segments.
 // With one segment only the full mode runs.
 //
-// Work split in a workgroup of two waves (64 state columns, a "slab"): wave w
-// owns chunk rows [32w, 32w+32) of Y, Z and o and state rows [K/2 w,
-// K/2 (w+1)).  Every A-operand fragment (k, q, W^T and A^ rows) belongs to
-// exactly one wave, which loads it straight into registers and reloads it for
-// the next chunk as soon as its products are issued.  Only the B operands
-// S and Z cross between the two waves, through LDS in fragment order
-// (accumulator tiles are B fragments, see gdr_device.hpp), with two barriers
-// per chunk.  The output is formed transposed, o^T = S^T q^T + Z^T A^T: the B
-// fragments of S and Z are also A fragments of S^T and Z^T, and the q and A^
-// fragments are B fragments of q^T and A^T, so no operand moves, and each
-// lane ends up with four consecutive columns of one o row (16-byte stores).
-// v arrives as 16-byte row pieces and reaches accumulator layout through a
-// per-wave LDS tile.  The fp32 state never leaves registers except at
-// segment ends.
+// Work split in a workgroup of NW = 4 waves (64 state columns, a "slab"):
+// wave w owns chunk rows [16w, 16w+16) of Y, Z and o and state rows
+// [K/4 w, K/4 (w+1)).  Every A-operand fragment (k, q, W^T and A^ rows)
+// belongs to exactly one wave, which loads it straight into registers.  The
+// next chunk's operands are double-buffered and their loads are issued one
+// at a time between the current chunk's products: issued in a burst they
+// stall the wave (in-order issue) while the memory pipeline drains them.
+// Only the B operands S and Z cross between waves, through LDS in fragment
+// order (accumulator tiles are B fragments, see gdr_device.hpp), with two
+// barriers per chunk.  The output is formed transposed,
+// o^T = S^T q^T + Z^T A^T: the B fragments of S and Z are also A fragments of
+// S^T and Z^T, and the q and A^ fragments are B fragments of q^T and A^T, so
+// no operand moves, and each lane ends up with four consecutive columns of
+// one o row (16-byte stores, issued at the top of the next chunk so that no
+// wait for loads also waits for them).  v arrives as 16-byte row pieces and
+// reaches accumulator layout through a per-wave LDS tile.  The fp32 state
+// never leaves registers except at segment ends.
 //
 // With one decay per row the k and q fragments come straight from the bf16
 // (or fp32) inputs; with per-channel decay they are the prep kernel's

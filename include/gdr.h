@@ -43,7 +43,10 @@
  * Numerics: with GDR_BF16 inputs the matrix products run on MFMA with fp16
  * operands and fp32 accumulation; the state, gamma, exponentials and o are
  * fp32.  bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
- * inputs every product runs in fp32.
+ * inputs every product runs in fp32.  With per-channel decay the decay is
+ * folded into fp16 operands, which grow as exp(sum of the positive g of a
+ * channel within one chunk): that sum must stay below about 8 (g <= 0, the
+ * usual log-decay, is always in range).
  */
 #ifndef GDR_H
 #define GDR_H
