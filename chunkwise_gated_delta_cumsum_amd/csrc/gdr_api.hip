@@ -257,7 +257,7 @@ ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
   a.scale = r.scale;
   a.seg_len = r.seg_len; a.nseg = r.nseg;
   a.seg_state = reinterpret_cast<float*>(base + L.seg);
-  a.phi = reinterpret_cast<float*>(base + L.phi);
+  a.phi = base + L.phi;
   a.eend = reinterpret_cast<float*>(base + L.eend);
   return a;
 }

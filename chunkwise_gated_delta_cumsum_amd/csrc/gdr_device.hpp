@@ -227,6 +227,19 @@ __device__ __forceinline__ bf16x8 frag_row_bf16(const uint16_t* row, int grp) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// A/B fragment of a row-contiguous workspace-type source: row[kslot(grp, i)].
+__device__ __forceinline__ half8 frag_row_ws(const _Float16* row, int grp) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 lo = *reinterpret_cast<const h4*>(row + 4 * grp);
+  const h4 hi = *reinterpret_cast<const h4*>(row + 16 + 4 * grp);
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ f32x8 frag_row_ws(const float* row, int grp) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 16 + 4 * grp);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Workspace fragment: 8 consecutive ws_t per lane.
 __device__ __forceinline__ half8 frag_ws(const _Float16* p) {
   return *reinterpret_cast<const half8*>(p);
@@ -280,8 +293,8 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 //        operands (rows c, k = d): [4][K/32][64][8] per value-head chunk.
 //        With one decay per row the scan reads q and k from the inputs.
 //   seg, phi, eend : sequence segments (when more than one): start states
-//        [B*HV][nseg][K*V], transitions [B*HV][nseg-1][K][K] and zero-start end
-//        states [B*HV][nseg-1][K*V], fp32.
+//        [B*HV][nseg][K*V] fp32, transitions [B*HV][nseg-1][K][K] in the
+//        workspace type and zero-start end states [B*HV][nseg-1][K*V] fp32.
 struct WsLayout {
   size_t wt, ah, rs, qh, kh, seg, phi, eend, total;
 };
@@ -302,7 +315,7 @@ __host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, i
   L.seg = L.phi = L.eend = off;
   if (nseg > 1) {
     L.seg = off; off = ws_align(off + nheads * nseg * (size_t)K * V * sizeof(float));
-    L.phi = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * K * sizeof(float));
+    L.phi = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * K * elem);
     L.eend = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * V * sizeof(float));
   }
   L.total = off;

@@ -22,6 +22,7 @@
 // 3-4 both kernels share; the per-key-channel (KDA) kernel is in
 // gdr_prep_kda.hpp.
 #pragma once
+#include <type_traits>
 #include "gdr_device.hpp"
 
 namespace gdr {
@@ -45,13 +46,20 @@ struct PrepArgs {
 };
 
 #ifdef GDR_PREP_PROFILE
+// phase timestamps of one chunk, kept in registers and written at the end so
+// that the marks themselves add no memory traffic to the phases
 __device__ long long gdr_prep_prof[16 * 4];
-#define GDR_PPROF(ph)                                                         \
-  do {                                                                        \
-    if (cid == 7 && lane == 0) gdr_prep_prof[(ph) * 4 + wave] = clock64();    \
+#define GDR_PPROF_DECL long long gdr_pt_[8] = {0, 0, 0, 0, 0, 0, 0, 0}
+#define GDR_PPROF(ph) gdr_pt_[ph] = clock64()
+#define GDR_PPROF_FLUSH                                                        \
+  do {                                                                         \
+    if (cid == 7 && lane == 0)                                                 \
+      for (int ph_ = 0; ph_ < 8; ++ph_) gdr_prep_prof[ph_ * 4 + wave] = gdr_pt_[ph_]; \
   } while (0)
 #else
+#define GDR_PPROF_DECL do {} while (0)
 #define GDR_PPROF(ph) do {} while (0)
+#define GDR_PPROF_FLUSH do {} while (0)
 #endif
 
 // XCD-aware placement of chunks: the value heads that share one q/k head get
@@ -70,35 +78,70 @@ __device__ __forceinline__ bool prep_block(int B, int H, int G, int N, int& b, i
 
 constexpr int kLP = kChunk + 4;   // row stride of the C x C fp32 LDS tiles
 
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ---- step 3: M^-1 by 16-row blocks ----------------------------------------
 // In: sL = strictly lower A_kk diag(beta) (= M - I), row-major, stride kLP;
 // the caller has synchronised after writing it.  Out: sMT = M^-T (row j holds
-// column j of M^-1), and the diagonal blocks of sL hold D_I = M_II^-1.
-// Ends with a workgroup barrier.
+// column j of M^-1, upper blocks zero), and the diagonal blocks of sL hold
+// D_I = M_II^-1.  Ends with a workgroup barrier.
+//   3a. wave I inverts its diagonal block by forward substitution (lane r
+//       computes column r of D_I);
+//   3b. wave J forms block column J of M^-1, X_IJ = -D_I sum_{m<I} L_Im X_mJ,
+//       keeping the X_mJ in registers: an accumulator tile is the B operand
+//       of a 16x16x16 product (k = its rows), so no tile goes through LDS
+//       until the wave writes its row block of M^-T.
+template <class P, int J>
+__device__ __forceinline__ void inverse_column(const float* sL, float* sMT, const float (&x)[16],
+                                               int r, int grp) {
+  constexpr int LP = kLP;
+  f32x4 X[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) X[I] = zero4();
+  X[J] = f32x4{x[4 * grp], x[4 * grp + 1], x[4 * grp + 2], x[4 * grp + 3]};   // D_J
+  static_for<J + 1, 4>([&](auto ic) {
+    constexpr int I = decltype(ic)::value;
+    f32x4 tacc = zero4();
+#pragma unroll
+    for (int m = J; m < I; ++m) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(sL + (16 * I + r) * LP + 16 * m + 4 * grp);
+      tacc = P::mma16(av, X[m], tacc);
+    }
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(sL + (16 * I + r) * LP + 16 * I + 4 * grp);
+    X[I] = -P::mma16(dv, tacc, zero4());
+  });
+  // row 16J + r of M^-T = column 16J + r of M^-1: X_IJ[4grp + j4][r] at
+  // columns 16I + 4grp + j4 (zero above the diagonal block)
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+    *reinterpret_cast<f32x4*>(sMT + (16 * J + r) * LP + 16 * I + 4 * grp) = X[I];
+}
+
 template <class P>
 __device__ __forceinline__ void unit_lower_inverse(float* sL, float* sMT, int tid, int wave,
                                                    int r, int grp) {
-  constexpr int C = kChunk, LP = kLP;
-  for (int i = tid * 4; i < C * LP; i += 256 * 4) *reinterpret_cast<f32x4*>(sMT + i) = zero4();
-  __syncthreads();
-  // 3a. wave `blk` inverts its diagonal block by forward substitution
+  constexpr int LP = kLP;
+  // 3a. column r of D = M_II^-1 for the wave's diagonal block I = wave
+  float x[16];
   {
-    const int blk = wave, j = r;
-    float* Lb = sL + (16 * blk) * LP + 16 * blk;
-    float x[16];
+    float* Lb = sL + (16 * wave) * LP + 16 * wave;
+    const int j = r;
+    // column-oriented forward substitution: once x[m] is final it is removed
+    // from every later row, so the dependent chain is 16 FMAs long instead of
+    // 120; each x[i] still subtracts the terms in the order m = 0, 1, ...
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = (i == j) ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) s -= Lb[i * LP + m] * x[m];
-      x[i] = s;
-    }
-    if (grp == 0) {
-      float* mt = sMT + (16 * blk + j) * LP + 16 * blk;  // row j of D^T
+    for (int m = 0; m < 15; ++m)
 #pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<f32x4*>(mt + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
-    }
+      for (int i = m + 1; i < 16; ++i) x[i] -= Lb[i * LP + m] * x[m];
     // D row-major into the (now unused) diagonal block of L, after every lane
     // of the wave has finished reading it
     __builtin_amdgcn_wave_barrier();
@@ -107,23 +150,12 @@ __device__ __forceinline__ void unit_lower_inverse(float* sL, float* sMT, int ti
       for (int i = 0; i < 16; ++i) Lb[i * LP + j] = x[i];
     }
   }
-  __syncthreads();
-  // 3b. wave J forms block column J of M^-1
-  {
-    const int J = wave;
-    for (int I = J + 1; I < 4; ++I) {
-      f32x4 tacc = zero4();
-      for (int m = J; m < I; ++m) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(sL + (16 * I + r) * LP + 16 * m + 4 * grp);
-        const f32x4 bv2 = *reinterpret_cast<const f32x4*>(sMT + (16 * J + r) * LP + 16 * m + 4 * grp);
-        tacc = P::mma16(av, bv2, tacc);
-      }
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(sL + (16 * I + r) * LP + 16 * I + 4 * grp);
-      const f32x4 x = P::mma16(dv, tacc, zero4());
-      // row j = 16J + r of M^-T holds column j of M^-1; this wave is its only
-      // writer and reader, so no barrier is needed until the next phase
-      *reinterpret_cast<f32x4*>(sMT + (16 * J + r) * LP + 16 * I + 4 * grp) = -x;
-    }
+  __syncthreads();   // every D_I is in sL
+  switch (wave) {
+    case 0: inverse_column<P, 0>(sL, sMT, x, r, grp); break;
+    case 1: inverse_column<P, 1>(sL, sMT, x, r, grp); break;
+    case 2: inverse_column<P, 2>(sL, sMT, x, r, grp); break;
+    default: inverse_column<P, 3>(sL, sMT, x, r, grp); break;
   }
   __syncthreads();
 }
@@ -215,6 +247,94 @@ __device__ __forceinline__ void dump_minv(float* out, const float* sMT, int tid)
   for (int e = tid; e < C * C; e += 256) out[e] = sMT[(e % C) * kLP + e / C];
 }
 
+// Step 2 for one decay per row, for wave W (a template argument, so every
+// tile, mask and table below is known at compile time).  Every wave has five
+// 16x16 tile jobs: the A_qk^T tiles (J, W) for J <= W, kept in registers as
+// the B operands of step 4b, then 4 - W of the A_kk tiles, written to sL.
+// The Gram products are exact bf16 x bf16 (or fp32) products; the decay
+// exp(gamma_i - gamma_j), beta and the scale are applied in fp32 per entry,
+// with a mask only on diagonal tiles.  The operands of job j+1 are read from
+// LDS while the products of job j run.
+template <int W, int K, class P>
+__device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typename P::in_t* sQ,
+                                           float* sL, const float* sGam, const float* sBeta,
+                                           float scale, int r, int grp, f32x4 (&aqT)[4]) {
+  using in_t = typename P::in_t;
+  using gfrag_t = std::conditional_t<P::kF32, f32x8, bf16x8>;
+  constexpr int KB = K / 32;
+  constexpr int KP = K + 16 / (int)sizeof(in_t);
+  constexpr int LP = kLP;
+  constexpr int TI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+  constexpr int TJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+  constexpr int FIRST = W == 0 ? 0 : W == 1 ? 4 : W == 2 ? 7 : 9;
+  // job j: (x block, y block, is A_qk^T)
+  auto jx = [](int j) { return j <= W ? j : TI[FIRST + j - W - 1]; };
+  auto jy = [](int j) { return j <= W ? W : TJ[FIRST + j - W - 1]; };
+
+  // gamma and beta of the rows this lane touches: rows 16X + 4grp + (0..3)
+  // of the accumulator and row 16X + r of the columns, for every block X
+  f32x4 g4[4], b4[4];
+  float g1[4], b1[4];
+#pragma unroll
+  for (int X = 0; X < 4; ++X) {
+    g4[X] = *reinterpret_cast<const f32x4*>(sGam + 16 * X + 4 * grp);
+    b4[X] = *reinterpret_cast<const f32x4*>(sBeta + 16 * X + 4 * grp);
+    g1[X] = sGam[16 * X + r];
+    b1[X] = sBeta[16 * X + r];
+  }
+
+  auto frag = [&](const in_t* row) -> gfrag_t {
+    if constexpr (P::kF32)
+      return frag_row_in(row, grp, P{});
+    else
+      return frag_row_bf16(row, grp);
+  };
+  auto load_job = [&](int j, gfrag_t (&fx)[KB], gfrag_t (&fy)[KB]) {
+    const in_t* ra = sK + (16 * jx(j) + r) * KP;
+    const in_t* rb = (j <= W ? sQ : sK) + (16 * jy(j) + r) * KP;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      fx[kb] = frag(ra + 32 * kb);
+      fy[kb] = frag(rb + 32 * kb);
+    }
+  };
+  gfrag_t cx[KB], cy[KB], nx[KB], ny[KB];
+  load_job(0, cx, cy);
+  static_for<0, 5>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int X = j <= W ? j : TI[FIRST + j - W - 1];
+    constexpr int Y = j <= W ? W : TJ[FIRST + j - W - 1];
+    if constexpr (j < 4) load_job(j + 1, nx, ny);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc = mma32(cx[kb], cy[kb], acc);
+    f32x4 val;
+    if constexpr (j <= W) {
+      // A_qk^T tile (X, W): rows c' = 16X + 4grp + j4 (k), column i = 16W + r (q)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float x = acc[j4] * b4[X][j4] * scale * __expf(g1[W] - g4[X][j4]);
+        val[j4] = (X < W || 4 * grp + j4 <= r) ? x : 0.f;
+      }
+      aqT[X] = val;
+    } else {
+      // A_kk tile (X, Y): rows i = 16X + 4grp + j4, column j = 16Y + r
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float x = acc[j4] * b1[Y] * __expf(g4[X][j4] - g1[Y]);
+        sL[(16 * X + 4 * grp + j4) * LP + 16 * Y + r] = (X > Y || 4 * grp + j4 > r) ? x : 0.f;
+      }
+    }
+    if constexpr (j < 4) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        cx[kb] = nx[kb];
+        cy[kb] = ny[kb];
+      }
+    }
+  });
+}
+
 // ---- the kernel for one decay per row --------------------------------------
 template <int K, class P, bool DUMP>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
@@ -248,6 +368,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   const int cid = (b * a.HV + hv) * a.N + n;
   const int T = a.T;
   const int t0 = n * C;
+  GDR_PPROF_DECL;
   GDR_PPROF(0);
 
   // ---- issue every global load of the chunk up front ----------------------
@@ -296,55 +417,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   __syncthreads();
   GDR_PPROF(1);
 
-  // ---- 2. decayed dots ----------------------------------------------------
-  // A_qk^T tiles (rows c' in block J, columns i in block w) for J <= w stay
-  // in this wave's registers; A_kk tiles go to LDS.  Work per wave: w+1 A_qk
-  // tiles and 4-w A_kk tiles.  The Gram products are exact bf16 x bf16 (or
-  // fp32) products; the decay exp(gamma_i - gamma_j) is applied in fp32 per
-  // entry, and only where j <= i.
+  // ---- 2. decayed dots (gram_tiles) ----------------------------------------
   f32x4 aqT[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) aqT[j] = zero4();
-  {
-    auto gram = [&](const in_t* xs, int I, const in_t* ys, int J) -> f32x4 {
-      f32x4 acc = zero4();
-      const in_t* ra = xs + (16 * I + r) * KP;
-      const in_t* rb = ys + (16 * J + r) * KP;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if constexpr (P::kF32)
-          acc = mma32(frag_row_in(ra + 32 * kb, grp, P{}), frag_row_in(rb + 32 * kb, grp, P{}), acc);
-        else
-          acc = mma32(frag_row_bf16(ra + 32 * kb, grp), frag_row_bf16(rb + 32 * kb, grp), acc);
-      }
-      return acc;
-    };
-
-    // A_qk^T = k q^T: tiles (J, w), rows c' (k), columns i (q)
-    for (int J = 0; J <= wave; ++J) {
-      const f32x4 acc = gram(sK, J, sQ, wave);
-      f32x4 val;
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int cp = 16 * J + 4 * grp + j4, i = 16 * wave + r;
-        val[j4] = (cp <= i) ? acc[j4] * sBeta[cp] * a.scale * __expf(sGam[i] - sGam[cp]) : 0.f;
-      }
-      aqT[J] = val;
-    }
-    // A_kk lower tiles, wave w takes 4-w of them
-    constexpr int TI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    const int first = (wave == 0) ? 0 : (wave == 1) ? 4 : (wave == 2) ? 7 : 9;
-    const int count = 4 - wave;
-    for (int tj = first; tj < first + count; ++tj) {
-      const int I = TI[tj], J = TJ[tj];
-      const f32x4 acc = gram(sK, I, sK, J);
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int i = 16 * I + 4 * grp + j4, j = 16 * J + r;
-        sL[i * LP + j] = (i > j) ? acc[j4] * sBeta[j] * __expf(sGam[i] - sGam[j]) : 0.f;
-      }
-    }
+  switch (wave) {
+    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
+    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
+    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
+    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
   }
 
   __syncthreads();   // sL complete
@@ -382,6 +463,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     if (tid < K) rs[64 + tid] = __expf(sGam[C - 1]);
   }
   GDR_PPROF(7);
+  GDR_PPROF_FLUSH;
 }
 
 }  // namespace gdr

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   const int i = 16 * I + r;                 // this lane's row in the chunk
   const int t = n * C + i;
   const bool valid = t < T;
+  GDR_PPROF_DECL;
   GDR_PPROF(0);
 
   // ---- loads: this lane's row, channels 32kb + 8grp + (0..7) ---------------
@@ -342,6 +343,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   GDR_PPROF(5);
   fold_aqk<P>(aqT, sMT, static_cast<ws_t*>(a.ah) + (size_t)cid * C * C, wave, lane, r, grp);
   GDR_PPROF(6);
+  GDR_PPROF_FLUSH;
 }
 
 }  // namespace gdr

@@ -64,7 +64,7 @@ struct ScanArgs {
   // segment p covers chunks [p * seg_len, min((p + 1) * seg_len, N))
   int seg_len, nseg;
   float* seg_state;  // start states of the segments, tile order [BH][nseg][K*V]
-  float* phi;        // transitions, row-major [BH][nseg-1][K][K]
+  void* phi;         // transitions, row-major [BH][nseg-1][K][K], workspace type
   float* eend;       // zero-start end states, tile order [BH][nseg-1][K*V]
 };
 
@@ -481,8 +481,9 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
           }
     }
   } else if constexpr (PHI) {
-    // Phi columns [64 sv, 64 sv + 64), row-major
-    float* dst = a.phi + ((size_t)bh * (a.nseg - 1) + p) * K * K;
+    // Phi columns [64 sv, 64 sv + 64), row-major, in the workspace type (the
+    // combine consumes Phi as MFMA operands of that type anyway)
+    ws_t* dst = static_cast<ws_t*>(a.phi) + ((size_t)bh * (a.nseg - 1) + p) * K * K;
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
 #pragma unroll
@@ -490,7 +491,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 16 * (SRT * w + st) + 4 * grp + j;
-          dst[(size_t)d * K + sv * BV + 16 * ct + r] = S[st][ct][j];
+          dst[(size_t)d * K + sv * BV + 16 * ct + r] = (ws_t)S[st][ct][j];
         }
   } else {
     float* dst = a.eend + ((size_t)bh * (a.nseg - 1) + p) * K * V;
@@ -545,6 +546,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
 template <int K, int V, class P>
 __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
   using frag_t = typename P::frag_t;
+  using ws_t = typename P::ws_t;
   constexpr int BV = kScanBV;
   constexpr int NSLAB = V / BV;
   constexpr int NCT = BV / 16;
@@ -562,21 +564,17 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
   const int nstep = a.nseg - 1;
 
   struct Ops {
-    f32x4 ph[SRT][KB][2];   // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
+    frag_t ph[SRT][KB];     // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
     f32x4 e[SRT][NCT];
   };
   auto load = [&](int p, Ops& op) {
-    const float* ph = a.phi + ((size_t)bh * nstep + p) * K * K;
+    const ws_t* ph = static_cast<const ws_t*>(a.phi) + ((size_t)bh * nstep + p) * K * K;
     const float* e = a.eend + ((size_t)bh * nstep + p) * K * V;
 #pragma unroll
     for (int st = 0; st < SRT; ++st) {
       const int d = 16 * (SRT * w + st) + r;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        op.ph[st][kb][0] = *reinterpret_cast<const f32x4*>(ph + (size_t)d * K + 32 * kb + 4 * grp);
-        op.ph[st][kb][1] =
-            *reinterpret_cast<const f32x4*>(ph + (size_t)d * K + 32 * kb + 16 + 4 * grp);
-      }
+      for (int kb = 0; kb < KB; ++kb) op.ph[st][kb] = frag_row_ws(ph + (size_t)d * K + 32 * kb, grp);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
         op.e[st][ct] = *reinterpret_cast<const f32x4*>(
@@ -621,7 +619,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
         const frag_t fb = sS[(kb * NCT + ct) * 64 + lane];
 #pragma unroll
         for (int st = 0; st < SRT; ++st)
-          S[st][ct] = mma32(P::make2(cur.ph[st][kb][0], cur.ph[st][kb][1]), fb, S[st][ct]);
+          S[st][ct] = mma32(cur.ph[st][kb], fb, S[st][ct]);
       }
     float* dst = a.seg_state + ((size_t)bh * a.nseg + p + 1) * K * V;
 #pragma unroll
