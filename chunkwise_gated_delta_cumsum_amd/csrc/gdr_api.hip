@@ -95,9 +95,9 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
 size_t nchunks(const Prob& r) { return (size_t)r.B * r.HV * r.N; }
 
 WsLayout layout(const Prob& r) {
-  // q/k fragments with the decay folded in exist only per channel; with one
-  // decay per row the scan reads q and k from the inputs
-  const size_t qk = r.perch ? nchunks(r) : 0;
+  // q/k fragments: per value head with the per-channel decay folded in, per
+  // query head (shared by its value heads) with one decay per row
+  const size_t qk = r.perch ? nchunks(r) : (size_t)r.B * r.H * r.N;
   return ws_layout(nchunks(r), qk, r.K, r.V, r.es, (size_t)r.B * r.HV, r.nseg);
 }
 

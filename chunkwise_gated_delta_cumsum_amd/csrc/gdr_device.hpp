@@ -289,9 +289,12 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 //   ah : A^ = A_qk M^-1 as an A operand (rows i, k = c): [4][2][64][8]
 //   rs : 256 fp32: [0..63] exp(gamma_c) (one decay per row; 1 per channel),
 //        [64..64+K) exp(gamma_last) per key channel
-//   qh, kh : per-channel decay only: q exp(gamma) scale and k exp(gamma) as A
-//        operands (rows c, k = d): [4][K/32][64][8] per value-head chunk.
-//        With one decay per row the scan reads q and k from the inputs.
+//   qh, kh : the scan's q and k operands as A fragments (rows c, k = d):
+//        [4][K/32][64][8] per chunk; lane (r, g) of fragment (ct, kb) holds
+//        key channels 32 kb + 8 g .. +7 of row 16 ct + r.  Per channel they
+//        are q exp(gamma) scale and k exp(gamma), one per value-head chunk;
+//        with one decay per row they are q and k themselves, converted to
+//        the workspace type, one per query-head chunk.
 //   seg, phi, eend : sequence segments (when more than one): start states
 //        [B*HV][nseg][K*V] fp32, transitions [B*HV][nseg-1][K][K] in the
 //        workspace type and zero-start end states [B*HV][nseg-1][K*V] fp32.
@@ -302,7 +305,7 @@ struct WsLayout {
 __host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // nchunks = B * HV * N value-head chunks; qkchunks = chunks that carry their
-// own q/k fragments (0 with one decay per row, nchunks per channel).
+// own q/k fragments (B * H * N with one decay per row, nchunks per channel).
 __host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, int K, int V,
                                               size_t elem, size_t nheads, int nseg) {
   WsLayout L;

@@ -417,6 +417,31 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   __syncthreads();
   GDR_PPROF(1);
 
+  // ---- q and k for the scan, in its fragment order -------------------------
+  // Read straight from the inputs, an MFMA fragment would touch 16 rows per
+  // 16 lanes, which the vector memory path serves at a quarter of its
+  // contiguous rate; here the rows already sit in LDS, so each query head's
+  // q and k are written once (by the first of its value heads) as fragments
+  // the scan loads with 16 contiguous bytes per lane.  Piece pc = (ct KB +
+  // kb) 64 + lane holds channels 32 kb + 8 (lane / 16) .. +7 of row
+  // 16 ct + lane % 16; tail rows are the zero rows of the LDS tile.
+  if (hv % (a.HV / a.H) == 0) {
+    using frag_t = typename P::frag_t;
+    constexpr int KB = K / 32;
+    const size_t qcid = ((size_t)b * a.H + h) * a.N + n;
+    ws_t* qd = static_cast<ws_t*>(a.qh) + qcid * C * K;
+    ws_t* kd = static_cast<ws_t*>(a.kh) + qcid * C * K;
+#pragma unroll
+    for (int pc = tid; pc < C * K / 8; pc += 256) {
+      const int ln = pc & 63, tkb = pc >> 6;
+      const int row = 16 * (tkb / KB) + (ln & 15), ch = 32 * (tkb % KB) + 8 * (ln >> 4);
+      *reinterpret_cast<frag_t*>(qd + (size_t)pc * 8) =
+          P::frag_from_raw(P::load_raw8(sQ + row * KP + ch));
+      *reinterpret_cast<frag_t*>(kd + (size_t)pc * 8) =
+          P::frag_from_raw(P::load_raw8(sK + row * KP + ch));
+    }
+  }
+
   // ---- 2. decayed dots (gram_tiles) ----------------------------------------
   f32x4 aqT[4];
 #pragma unroll

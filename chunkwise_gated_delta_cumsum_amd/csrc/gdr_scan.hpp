@@ -33,14 +33,20 @@
 // o^T = S^T q^T + Z^T A^T: the B fragments of S and Z are also A fragments of
 // S^T and Z^T, and the q and A^ fragments are B fragments of q^T and A^T, so
 // no operand moves, and each lane ends up with four consecutive columns of
-// one o row (16-byte stores, issued at the top of the next chunk so that no
-// wait for loads also waits for them).  v arrives as 16-byte row pieces and
-// reaches accumulator layout through a per-wave LDS tile.  The fp32 state
-// never leaves registers except at segment ends.
+// one o row.  Those rows pass through a per-wave LDS area so that they leave
+// as whole 256-byte rows, stored at the end of the chunk's step once every
+// load of the step is issued (so no wait for loads also waits for them); v
+// arrives as 16-byte row pieces and reaches accumulator layout through a
+// per-wave LDS tile, filled at the end of the step before.  The LDS work
+// that belongs to no product thus sits after the last product of a step
+// instead of between the barrier and the first.  The fp32 state never
+// leaves registers except at segment ends.
 //
-// With one decay per row the k and q fragments come straight from the bf16
-// (or fp32) inputs; with per-channel decay they are the prep kernel's
-// k exp(gamma) and q exp(gamma) scale.
+// Every global operand is stored in the order its lanes consume it, 16
+// contiguous bytes per lane: the vector memory path serves a 16-lane access
+// that touches 16 rows at a quarter of its contiguous rate.  The k and q
+// fragments are the prep kernel's copies (q and k with one decay per row,
+// k exp(gamma) and q exp(gamma) scale per channel).
 #pragma once
 #include <type_traits>
 #include "gdr_device.hpp"
@@ -64,19 +70,29 @@ struct ScanArgs {
   // segment p covers chunks [p * seg_len, min((p + 1) * seg_len, N))
   int seg_len, nseg;
   float* seg_state;  // start states of the segments, tile order [BH][nseg][K*V]
-  void* phi;         // transitions, row-major [BH][nseg-1][K][K], workspace type
+  void* phi;         // transitions [BH][nseg-1], each K x K in A-fragment order
+                     // [K/16 row tiles][K/32 k blocks][64 lanes][8], workspace type
   float* eend;       // zero-start end states, tile order [BH][nseg-1][K*V]
 };
 
+#ifdef GDR_COMBINE_PROFILE
+__device__ long long gdr_comb_prof[32 * 5 * 4];
+#endif
 #ifdef GDR_SCAN_PROFILE
-__device__ long long gdr_scan_prof[64 * 8 * 4];
-#define GDR_PROF(ph)                                                               \
+// clock marks of one chunk step, kept in registers and written out at the
+// end of the step (a store per mark would add waits of its own)
+__device__ long long gdr_scan_prof[64 * 16 * 4];
+#define GDR_PROF_DECL long long pt_[16] = {}
+#define GDR_PROF(ph) pt_[ph] = clock64()
+#define GDR_PROF_FLUSH                                                             \
   do {                                                                             \
     if (MODE == kScanFull && bh == 0 && p == 0 && sv == 0 && lane == 0 && n < 64)   \
-      gdr_scan_prof[(n * 8 + (ph)) * 4 + w] = clock64();                           \
+      for (int i_ = 0; i_ < 16; ++i_) gdr_scan_prof[(n * 16 + i_) * 4 + w] = pt_[i_]; \
   } while (0)
 #else
+#define GDR_PROF_DECL do {} while (0)
 #define GDR_PROF(ph) do {} while (0)
+#define GDR_PROF_FLUSH do {} while (0)
 #endif
 
 constexpr int kScanFull = 0;
@@ -90,6 +106,15 @@ constexpr int kCombineWaves = 4;
 // prefetch) stay in flight.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for_scan(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for_scan<B + 1, E>(f);
+  }
 }
 
 // Half of a fragment (4 consecutive k slots) in LDS.
@@ -124,20 +149,22 @@ __device__ __forceinline__ size_t state_tile(int sv, int dt, int ct) {
   return (((size_t)sv * (K / 16) + dt) * (kScanBV / 16) + ct) * 256;
 }
 
+// Bytes of one wave's staging area for its fp32 o rows (full mode only).
+template <int MODE>
+constexpr int scan_stage_bytes() {
+  return MODE == kScanFull ? (kChunk / kScanWaves) * (kScanBV * 4 + 16) : 16;
+}
+
 // One wave of a scan workgroup.  W (the wave index) and PHI (chain mode:
 // transition slab, identity start and no v) are template arguments so that
 // every choice between waves and slab kinds folds at compile time.
 template <int K, int V, bool PERCH, class P, int MODE, int NW, int W, bool PHI>
 __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t* sS,
                                           typename P::frag_t* sZ, typename P::in_t* sVw,
-                                          int unit, int sv) {
+                                          unsigned char* stg, int unit, int sv) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
   using ws_t = typename P::ws_t;
-  using raw_t = typename P::raw_t;
-  // k / q operands as held between load and use: workspace fragments with
-  // per-channel decay, raw input elements otherwise
-  using kq_t = std::conditional_t<PERCH, frag_t, raw_t>;
   constexpr bool FULL = MODE == kScanFull;
   constexpr int C = kChunk;
   constexpr int BV = kScanBV;
@@ -155,6 +182,13 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   constexpr int w = W;
   // k blocks of c (32 rows) that meet this wave's rows in A^ (lower triangular)
   constexpr int AKB = (CR * (w + 1) + 31) / 32;
+  // o rows leave through the wave's staging area: fp32, BV columns, padded
+  // so that the 16 rows of an accumulator tile land on distinct banks
+  constexpr int ORB = BV * 4 + 16;
+  constexpr int OLPR = BV * 4 / 16;            // lanes per o row
+  constexpr int ORPI = 64 / OLPR;              // o rows per store instruction
+  constexpr int ONI = CR / ORPI;               // o store instructions
+  static_assert(CR % ORPI == 0, "o row staging shape");
 
   const int nsegu = FULL ? a.nseg : a.nseg - 1;
   const int bh = unit / nsegu, p = unit % nsegu;
@@ -180,36 +214,26 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   // flight is conservative) finds a load issued late.
   u32x4 vr[VNI];
   struct WA {
-    kq_t kf[CT][KB], qf[CT][KB];
+    frag_t kf[CT][KB], qf[CT][KB];
     frag_t wf[SRT][2], af[CT][2];
     f32x4 eg[CT];                        // exp(gamma), rows CR w + 16ct + 4grp + j
     float ego[CT];                       // exp(gamma), row CR w + 16ct + r
     f32x4 dl[PERCH ? SRT : 1];           // exp(gamma_last) per state row (one value
                                          // for every row with scalar decay)
   };
-  auto kq_load = [&](const void* base, const ws_t* wsb, int n, int ct, int kb) -> kq_t {
-    if constexpr (PERCH) {
-      const size_t cid = (size_t)bh * a.N + n;
-      return frag_ws(wsb + ((cid * 4 + CT * w + ct) * KB + kb) * 512 + lane * 8);
-    } else {
-      const int t = min(n * C + CR * w + 16 * ct + r, T - 1);
-      const in_t* row = static_cast<const in_t*>(base) + (((size_t)b * T + t) * a.H + h) * K;
-      return P::load_raw8(row + 32 * kb + 8 * grp);
-    }
-  };
-  // Rows past T (read as row T-1) need no mask: their Z rows meet zero rows
-  // of W^ and zero columns of A^ (beta = 0 there), and their o is not stored.
-  auto kq_frag = [&](const kq_t& x) -> frag_t {
-    if constexpr (PERCH)
-      return x;
-    else
-      return P::frag_from_raw(x);
+  // k / q fragments from the prep kernel's copies, 16 contiguous bytes per
+  // lane: per value head with per-channel decay, per query head otherwise.
+  // Rows past T are zero there; their Z rows meet zero rows of W^ and zero
+  // columns of A^ (beta = 0 there), and their o is not stored.
+  const size_t qkb = PERCH ? (size_t)bh * a.N : ((size_t)b * a.H + h) * a.N;
+  auto kq_load = [&](const ws_t* wsb, int n, int ct, int kb) -> frag_t {
+    return frag_ws(wsb + (((qkb + n) * 4 + CT * w + ct) * KB + kb) * 512 + lane * 8);
   };
   auto load_v = [&](int n) {
     if constexpr (!PHI) {
 #pragma unroll
       for (int i = 0; i < VNI; ++i) {
-        // tail rows read row T-1 (see kq_frag)
+        // tail rows read row T-1 (see kq_load_raw)
         const int t = min(n * C + CR * w + VRI * i + lane / VPR, T - 1);
         vr[i] = *reinterpret_cast<const u32x4*>(
             vg + (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % VPR) * VVEC);
@@ -219,9 +243,10 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   // The next chunk's operands as a list of load items, issued one at a time
   // between the products of the current chunk: a burst of them would stall
   // the wave at issue (in order) while the memory pipeline drains it.
+  constexpr int NKQ = CT * KB;                  // load items per k / q operand
   constexpr int IT_K = 0;
-  constexpr int IT_Q = IT_K + CT * KB;
-  constexpr int IT_W = IT_Q + (FULL ? CT * KB : 0);
+  constexpr int IT_Q = IT_K + NKQ;
+  constexpr int IT_W = IT_Q + (FULL ? NKQ : 0);
   constexpr int IT_A = IT_W + SRT * 2;
   constexpr int IT_R = IT_A + (FULL ? CT * AKB : 0);
   constexpr int NITEMS = IT_R + 1;
@@ -230,11 +255,11 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     const float* rs = a.rs + cid * 256;
     if (i < IT_Q) {
       const int ct = (i - IT_K) / KB, kb = (i - IT_K) % KB;
-      x.kf[ct][kb] = kq_load(a.k, static_cast<const ws_t*>(a.kh), n, ct, kb);
+      x.kf[ct][kb] = kq_load(static_cast<const ws_t*>(a.kh), n, ct, kb);
     } else if (i < IT_W) {
       if constexpr (FULL) {
         const int ct = (i - IT_Q) / KB, kb = (i - IT_Q) % KB;
-        x.qf[ct][kb] = kq_load(a.q, static_cast<const ws_t*>(a.qh), n, ct, kb);
+        x.qf[ct][kb] = kq_load(static_cast<const ws_t*>(a.qh), n, ct, kb);
       }
     } else if (i < IT_A) {
       const int st = (i - IT_W) / 2, kb = (i - IT_W) % 2;
@@ -303,30 +328,9 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
         }
   }
 
-  load_v(n0);
-
-  // o^T of a chunk is stored at the top of the next iteration (or after the
-  // loop), after the wait for the loads in flight, so that wait never covers
-  // freshly issued stores
-  f32x4 OT[NCT][CT];
-  auto store_o = [&](int n) {
-    // lane holds o[row CR w + 16 c2 + r][columns v0 + 16ct + 4grp .. +3]
-#pragma unroll
-    for (int c2 = 0; c2 < CT; ++c2) {
-      const int t = n * C + CR * w + 16 * c2 + r;
-      if (t < T) {
-        float* orow = a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 + 4 * grp;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(orow + 16 * ct) = OT[ct][c2];
-      }
-    }
-  };
-
-  auto step = [&](int n, const WA& cur, WA& nxt) {
-    const int nn = min(n + 1, n1 - 1);   // the last chunk reloads itself
-    GDR_PROF(0);
-    // v rows of this wave into its LDS tile, the previous chunk's o, then the
-    // next chunk's v
+  // v rows of this wave into its LDS tile (the first chunk's here, every
+  // later chunk's at the end of the step before it)
+  auto stage_v = [&]() {
     if constexpr (!PHI) {
 #pragma unroll
       for (int i = 0; i < VNI; ++i) {
@@ -334,10 +338,44 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
         *reinterpret_cast<u32x4*>(sVw + row * VP + (lane % VPR) * VVEC) = vr[i];
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (FULL) {
-      if (n > n0) store_o(n - 1);
+  };
+  load_v(n0);
+  stage_v();
+
+  // o^T of a chunk leaves at the end of its step, after its last product and
+  // after every load of the step is issued (so that no later wait for those
+  // loads also waits for the stores): its accumulator tiles (lane: o row
+  // CR w + 16 c2 + r, columns v0 + 16ct + 4grp .. +3) go to the staging area
+  // as fp32 rows and come back as whole-row pieces.
+  f32x4 OT[NCT][CT];
+  f32x4 orow_v[ONI];
+  auto stage_o = [&]() {
+#pragma unroll
+    for (int c2 = 0; c2 < CT; ++c2)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        *reinterpret_cast<f32x4*>(stg + (16 * c2 + r) * ORB + (16 * ct + 4 * grp) * 4) =
+            OT[ct][c2];
+#pragma unroll
+    for (int i = 0; i < ONI; ++i)
+      orow_v[i] = *reinterpret_cast<const f32x4*>(stg + (ORPI * i + lane / OLPR) * ORB +
+                                                 (lane % OLPR) * 16);
+  };
+  auto store_o = [&](int n) {
+#pragma unroll
+    for (int i = 0; i < ONI; ++i) {
+      const int t = n * C + CR * w + ORPI * i + lane / OLPR;
+      if (t < T)
+        *reinterpret_cast<f32x4*>(a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 +
+                                  (lane % OLPR) * 4) = orow_v[i];
     }
+  };
+
+  auto step = [&](int n, const WA& cur, WA& nxt) {
+    const int nn = min(n + 1, n1 - 1);   // the last chunk reloads itself
+    GDR_PROF_DECL;
+    GDR_PROF(0);
+    // the next chunk's v (into the LDS tile at the end of this step)
     if constexpr (!PHI) load_v(nn);
     // this wave's state rows as halves of the B fragments of S
 #pragma unroll
@@ -347,6 +385,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
       for (int ct = 0; ct < NCT; ++ct)
         store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
     }
+    GDR_PROF(11);
     lds_barrier();
     GDR_PROF(1);
     int item = 0;
@@ -375,8 +414,8 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
         frag_t fk[CT], fq[CT];
 #pragma unroll
         for (int c2 = 0; c2 < CT; ++c2) {
-          fk[c2] = kq_frag(cur.kf[c2][kb]);
-          if constexpr (FULL) fq[c2] = kq_frag(cur.qf[c2][kb]);
+          fk[c2] = cur.kf[c2][kb];
+          if constexpr (FULL) fq[c2] = cur.qf[c2][kb];
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -452,9 +491,19 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     }
 #pragma unroll
     for (; item < NITEMS; ++item) load_item(item, nn, nxt);
+    GDR_PROF(12);
+    // this chunk's o, then the next chunk's v rows into the LDS tile (this
+    // chunk's were last read for Z)
+    if constexpr (FULL) {
+      stage_o();
+      GDR_PROF(9);
+      store_o(n);
+    }
+    stage_v();
     GDR_PROF(4);
 
     GDR_PROF(5);
+    GDR_PROF_FLUSH;
   };
 
   // two chunks per iteration with the operand buffers in swapped roles
@@ -468,7 +517,6 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   if (n < n1) step(n, bufA, bufB);
 
   if constexpr (FULL) {
-    store_o(n1 - 1);
     if (a.sT && p == a.nseg - 1) {
 #pragma unroll
       for (int st = 0; st < SRT; ++st)
@@ -481,18 +529,24 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
           }
     }
   } else if constexpr (PHI) {
-    // Phi columns [64 sv, 64 sv + 64), row-major, in the workspace type (the
-    // combine consumes Phi as MFMA operands of that type anyway)
+    // Phi columns [64 sv, 64 sv + 64) in the workspace type, in the order in
+    // which the combine reads them as A fragments: element (row d, column c)
+    // goes to fragment (row tile d / 16, k block c / 32), lane
+    // d % 16 + 16 g, slot i with c % 32 = kslot(g, i).  Here c % 32 =
+    // 16 (ct & 1) + r, so g = r / 4 and i = 4 (ct & 1) + r % 4.
     ws_t* dst = static_cast<ws_t*>(a.phi) + ((size_t)bh * (a.nseg - 1) + p) * K * K;
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int kb = (sv * BV + 16 * ct) / 32;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int d = 16 * (SRT * w + st) + 4 * grp + j;
-          dst[(size_t)d * K + sv * BV + 16 * ct + r] = (ws_t)S[st][ct][j];
+          const int fl = 4 * grp + j + 16 * (r >> 2);
+          dst[(((size_t)(SRT * w + st) * KB + kb) * 64 + fl) * 8 + 4 * (ct & 1) + (r & 3)] =
+              (ws_t)S[st][ct][j];
         }
+      }
   } else {
     float* dst = a.eend + ((size_t)bh * (a.nseg - 1) + p) * K * V;
 #pragma unroll
@@ -518,6 +572,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   __shared__ frag_t sS[KB * NCT * 64];                // B fragments of S
   __shared__ frag_t sZ[2 * NCT * 64];                 // B fragments of Z
   __shared__ __attribute__((aligned(16))) in_t sV[NW][(64 / NW) * VP];
+  __shared__ __attribute__((aligned(16))) unsigned char sStg[NW][scan_stage_bytes<MODE>()];
 
   const int nsegu = FULL ? a.nseg : a.nseg - 1;       // segments handled by this pass
   int unit, sv;
@@ -525,12 +580,12 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   const int wv = wave_id();
   auto run = [&](auto phi) {
     constexpr bool PHI = decltype(phi)::value;
-    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, NW, 0, PHI>(a, sS, sZ, sV[0], unit, sv);
+    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, NW, 0, PHI>(a, sS, sZ, sV[0], sStg[0], unit, sv);
     if constexpr (NW > 1)
-      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, NW, 1, PHI>(a, sS, sZ, sV[1], unit, sv);
+      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, NW, 1, PHI>(a, sS, sZ, sV[1], sStg[1], unit, sv);
     if constexpr (NW > 2) {
-      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, NW, 2, PHI>(a, sS, sZ, sV[2], unit, sv);
-      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, NW, 3, PHI>(a, sS, sZ, sV[3], unit, sv);
+      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, NW, 2, PHI>(a, sS, sZ, sV[2], sStg[2], unit, sv);
+      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, NW, 3, PHI>(a, sS, sZ, sV[3], sStg[3], unit, sv);
     }
   };
   if (FULL || sv >= K / kScanBV)
@@ -567,14 +622,16 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
     frag_t ph[SRT][KB];     // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
     f32x4 e[SRT][NCT];
   };
+  // both operands are stored in the order the lanes consume them: 16
+  // contiguous bytes per lane
   auto load = [&](int p, Ops& op) {
     const ws_t* ph = static_cast<const ws_t*>(a.phi) + ((size_t)bh * nstep + p) * K * K;
     const float* e = a.eend + ((size_t)bh * nstep + p) * K * V;
 #pragma unroll
     for (int st = 0; st < SRT; ++st) {
-      const int d = 16 * (SRT * w + st) + r;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) op.ph[st][kb] = frag_row_ws(ph + (size_t)d * K + 32 * kb, grp);
+      for (int kb = 0; kb < KB; ++kb)
+        op.ph[st][kb] = frag_ws(ph + (((size_t)(SRT * w + st) * KB + kb) * 64 + lane) * 8);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
         op.e[st][ct] = *reinterpret_cast<const f32x4*>(
@@ -599,7 +656,20 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
         }
   }
 
+#ifdef GDR_COMBINE_PROFILE
+  long long cpt[5];
+#define GDR_CPROF(i) cpt[i] = clock64()
+#define GDR_CFLUSH(p)                                                              \
+  do {                                                                             \
+    if (bh == 0 && sv == 0 && lane == 0 && (p) < 32)                               \
+      for (int i_ = 0; i_ < 5; ++i_) gdr_comb_prof[((p) * 5 + i_) * 4 + w] = cpt[i_]; \
+  } while (0)
+#else
+#define GDR_CPROF(i) do {} while (0)
+#define GDR_CFLUSH(p) do {} while (0)
+#endif
   auto step = [&](int p, const Ops& cur) {
+    GDR_CPROF(0);
 #pragma unroll
     for (int st = 0; st < SRT; ++st) {
       const int tile = SRT * w + st;
@@ -608,6 +678,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
         store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
     }
     lds_barrier();
+    GDR_CPROF(1);
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
 #pragma unroll
@@ -621,6 +692,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
         for (int st = 0; st < SRT; ++st)
           S[st][ct] = mma32(cur.ph[st][kb], fb, S[st][ct]);
       }
+    GDR_CPROF(2);
     float* dst = a.seg_state + ((size_t)bh * a.nseg + p + 1) * K * V;
 #pragma unroll
     for (int st = 0; st < SRT; ++st)
@@ -628,19 +700,31 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
       for (int ct = 0; ct < NCT; ++ct)
         *reinterpret_cast<f32x4*>(dst + state_tile<K>(sv, SRT * w + st, ct) + lane * 4) =
             S[st][ct];
+    GDR_CPROF(3);
     lds_barrier();   // every wave has read sS before it is rewritten
+    GDR_CPROF(4);
+    GDR_CFLUSH(p);
   };
 
-  Ops bufA, bufB;
-  load(0, bufA);
-  int p = 0;
-  for (; p + 1 < nstep; p += 2) {
-    load(p + 1, bufB);
-    step(p, bufA);
-    if (p + 2 < nstep) load(p + 2, bufA);
-    step(p + 1, bufB);
+  // A ring of NB operand buffers, filled NB - 1 steps ahead (each step is
+  // short, so one step of lead does not cover the load latency); the loop is
+  // unrolled NB times so every buffer index is a compile-time constant.
+  constexpr int NB = 3;
+  Ops buf[NB];
+  static_for_scan<0, NB - 1>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (i < nstep) load(i, buf[i]);
+  });
+  for (int p0 = 0; p0 < nstep; p0 += NB) {
+    static_for_scan<0, NB>([&](auto bc) {
+      constexpr int bi = decltype(bc)::value;
+      const int p = p0 + bi;
+      if (p < nstep) {
+        if (p + NB - 1 < nstep) load(p + NB - 1, buf[(bi + NB - 1) % NB]);
+        step(p, buf[bi]);
+      }
+    });
   }
-  if (p < nstep) step(p, bufA);
 }
 
 }  // namespace gdr

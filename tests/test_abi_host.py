@@ -73,7 +73,8 @@ def base(**kw):
 def test_workspace_size(lib):
     p = base()
     n = 1 * 4 * 2   # B * HV * ceil(100 / 64)
-    expect_min = n * (128 * 64 * 2 + 64 * 64 * 2 + 256 * 4)
+    nq = 1 * 2 * 2  # B * H * ceil(100 / 64): q and k fragments per query head
+    expect_min = n * (128 * 64 * 2 + 64 * 64 * 2 + 256 * 4) + nq * 2 * (64 * 128 * 2)
     assert gdr.workspace_size(p) >= expect_min
     assert gdr.workspace_size(base(per_channel=True)) > gdr.workspace_size(p)
     assert gdr.workspace_size(base(dtype="fp32")) > gdr.workspace_size(p)
