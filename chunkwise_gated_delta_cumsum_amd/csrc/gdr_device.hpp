@@ -18,6 +18,20 @@
 
 namespace gdr {
 
+#ifdef GDR_WG_TIMES
+// Start and end of every workgroup on the chip-wide constant-rate clock
+// (profiling builds only): [kernel kind][block][2], kind 0 prep, 1 chain
+// pass, 2 combine, 3 full pass.
+__device__ long long gdr_wg_times[4][32768][2];
+#define GDR_WGT(kind, which)                                                      \
+  do {                                                                            \
+    if (threadIdx.x == 0 && blockIdx.x < 32768)                                   \
+      gdr_wg_times[kind][blockIdx.x][which] = wall_clock64();                     \
+  } while (0)
+#else
+#define GDR_WGT(kind, which) do {} while (0)
+#endif
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -252,21 +266,24 @@ __device__ __forceinline__ f32x8 frag_ws(const float* p) {
   for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[4 + i] = hi[i]; }
   return f;
 }
+// Workspace writes are streamed (non-temporal): the next kernel reads them
+// from another XCD's L2 or from memory anyway, and lines that stay dirty in
+// this L2 only lengthen the write-back at the kernel boundary.
 __device__ __forceinline__ void store_ws(_Float16* p, f32x4 lo, f32x4 hi) {
   half8 f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) { f[i] = (_Float16)lo[i]; f[4 + i] = (_Float16)hi[i]; }
-  *reinterpret_cast<half8*>(p) = f;
+  __builtin_nontemporal_store(f, reinterpret_cast<half8*>(p));
 }
 __device__ __forceinline__ void store_ws(float* p, f32x4 lo, f32x4 hi) {
-  *reinterpret_cast<f32x4*>(p) = lo;
-  *reinterpret_cast<f32x4*>(p + 4) = hi;
+  __builtin_nontemporal_store(lo, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(hi, reinterpret_cast<f32x4*>(p + 4));
 }
 __device__ __forceinline__ void store_ws8(_Float16* p, const float* v) {
   half8 f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = (_Float16)v[i];
-  *reinterpret_cast<half8*>(p) = f;
+  __builtin_nontemporal_store(f, reinterpret_cast<half8*>(p));
 }
 __device__ __forceinline__ void store_ws8(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};

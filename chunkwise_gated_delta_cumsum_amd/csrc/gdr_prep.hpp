@@ -370,6 +370,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   const int t0 = n * C;
   GDR_PPROF_DECL;
   GDR_PPROF(0);
+  GDR_WGT(0, 0);
 
   // ---- issue every global load of the chunk up front ----------------------
   const in_t* qg = static_cast<const in_t*>(a.q);
@@ -435,10 +436,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     for (int pc = tid; pc < C * K / 8; pc += 256) {
       const int ln = pc & 63, tkb = pc >> 6;
       const int row = 16 * (tkb / KB) + (ln & 15), ch = 32 * (tkb % KB) + 8 * (ln >> 4);
-      *reinterpret_cast<frag_t*>(qd + (size_t)pc * 8) =
-          P::frag_from_raw(P::load_raw8(sQ + row * KP + ch));
-      *reinterpret_cast<frag_t*>(kd + (size_t)pc * 8) =
-          P::frag_from_raw(P::load_raw8(sK + row * KP + ch));
+      __builtin_nontemporal_store(P::frag_from_raw(P::load_raw8(sQ + row * KP + ch)),
+                                  reinterpret_cast<frag_t*>(qd + (size_t)pc * 8));
+      __builtin_nontemporal_store(P::frag_from_raw(P::load_raw8(sK + row * KP + ch)),
+                                  reinterpret_cast<frag_t*>(kd + (size_t)pc * 8));
     }
   }
 
@@ -489,6 +490,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   }
   GDR_PPROF(7);
   GDR_PPROF_FLUSH;
+  GDR_WGT(0, 1);
 }
 
 }  // namespace gdr

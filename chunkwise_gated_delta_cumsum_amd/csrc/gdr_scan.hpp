@@ -366,8 +366,9 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     for (int i = 0; i < ONI; ++i) {
       const int t = n * C + CR * w + ORPI * i + lane / OLPR;
       if (t < T)
-        *reinterpret_cast<f32x4*>(a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 +
-                                  (lane % OLPR) * 4) = orow_v[i];
+        // streamed: o is not read again on the device by this path
+        __builtin_nontemporal_store(orow_v[i], reinterpret_cast<f32x4*>(
+            a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % OLPR) * 4));
     }
   };
 
@@ -578,6 +579,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   int unit, sv;
   if (!unit_block(a.B * a.HV * nsegu, NSLAB, unit, sv)) return;
   const int wv = wave_id();
+  GDR_WGT(FULL ? 3 : 1, 0);
   auto run = [&](auto phi) {
     constexpr bool PHI = decltype(phi)::value;
     if (wv == 0) scan_wave<K, V, PERCH, P, MODE, NW, 0, PHI>(a, sS, sZ, sV[0], sStg[0], unit, sv);
@@ -592,6 +594,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
     run(std::false_type{});
   else if constexpr (!FULL)
     run(std::true_type{});
+  GDR_WGT(FULL ? 3 : 1, 1);
 }
 
 // Combine pass: S_{p+1} = Phi_p S_p + E_p over the segments of one head,
@@ -617,6 +620,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
   const int r = lane & 15, grp = lane >> 4;
   const int v0 = sv * BV;
   const int nstep = a.nseg - 1;
+  GDR_WGT(2, 0);
 
   struct Ops {
     frag_t ph[SRT][KB];     // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
@@ -725,6 +729,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
       }
     });
   }
+  GDR_WGT(2, 1);
 }
 
 }  // namespace gdr
