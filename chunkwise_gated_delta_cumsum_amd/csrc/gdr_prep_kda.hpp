@@ -68,11 +68,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   constexpr size_t TAB_BYTES = (size_t)(4 + 4 + NPAIR) * K * sizeof(float);
   constexpr size_t MT_BYTES = (size_t)C * LP * sizeof(float);
   constexpr size_t X_BYTES = KE_BYTES + TAB_BYTES > MT_BYTES ? KE_BYTES + TAB_BYTES : MT_BYTES;
-  // earlier-row fragments of blocks 0..2 and the per-channel tables; M^-T later
-  __shared__ __attribute__((aligned(16))) char sX[X_BYTES];
-  // beta k exp(gamma_last - gamma), row-major (c, d), for W^
-  __shared__ __attribute__((aligned(16))) ws_t sSK[C * SP];
-  __shared__ __attribute__((aligned(16))) float sL[C * LP];    // A_kk beta (strict); D_I later
+  constexpr size_t SK_BYTES = (size_t)C * SP * sizeof(ws_t);
+  constexpr size_t L_BYTES = (size_t)C * LP * sizeof(float);
+  // Loads: each wave's 16 rows of g, q and k arrive as whole rows (16 bytes
+  // per lane, a row per 16..32 lanes) and pass through a per-wave staging
+  // area into the row-per-lane layout below; read straight into that layout,
+  // each 16-lane group would touch 16 rows, which the vector memory path
+  // serves at a quarter of its contiguous rate.  Padded staging rows put the
+  // 16 rows of one read on distinct banks.
+  constexpr int GSR = K * 4 + 16;                           // staged g row (bytes)
+  constexpr int QSR = K * (int)sizeof(in_t) + 16;           // staged q / k row
+  constexpr int STG = 16 * GSR > 32 * QSR ? 16 * GSR : 32 * QSR;
+  static_assert(4 * (size_t)STG <= X_BYTES + SK_BYTES + L_BYTES, "staging fits the LDS block");
+  // one LDS block, in phases: the load staging first; then sX = earlier-row
+  // fragments of blocks 0..2 and the per-channel tables (M^-T later), sSK =
+  // beta k exp(gamma_last - gamma), row-major (c, d), for W^, and sL = A_kk
+  // beta (strict; D_I later)
+  __shared__ __attribute__((aligned(16))) char sBig[X_BYTES + SK_BYTES + L_BYTES];
+  char* sX = sBig;
+  ws_t* sSK = reinterpret_cast<ws_t*>(sBig + X_BYTES);
+  float* sL = reinterpret_cast<float*>(sBig + X_BYTES + SK_BYTES);
   __shared__ __attribute__((aligned(16))) float sTot[4 * K];   // s at row 15 of each block
   __shared__ __attribute__((aligned(16))) float sMid[4 * K];   // s at row 7 of each block
   __shared__ float sBeta[C];
@@ -97,22 +112,52 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   GDR_PPROF(0);
 
   // ---- loads: this lane's row, channels 32kb + 8grp + (0..7) ---------------
+  // Rows past T read row T-1; the valid masks below zero their g and beta.
   raw_t qr[KB], kr[KB];
   f32x4 glo[KB], ghi[KB];
   float bv;
   {
-    const int tt = min(t, T - 1);
-    const in_t* qrow = static_cast<const in_t*>(a.q) + (((size_t)b * T + tt) * a.H + h) * K;
-    const in_t* krow = static_cast<const in_t*>(a.k) + (((size_t)b * T + tt) * a.H + h) * K;
-    const float* grow = a.g + (((size_t)b * T + tt) * a.HV + hv) * K;
+    constexpr int GLPR = K * 4 / 16, GRPI = 64 / GLPR, GNI = 16 / GRPI;
+    constexpr int QLPR = K * (int)sizeof(in_t) / 16, QRPI = 64 / QLPR, QNI = 16 / QRPI;
+    static_assert(GRPI * GNI == 16 && QRPI * QNI == 16, "whole rows per load instruction");
+    u32x4 graw[GNI], qraw[QNI], kraw[QNI];
+#pragma unroll
+    for (int j = 0; j < GNI; ++j) {
+      const int tt = min(n * C + 16 * I + GRPI * j + lane / GLPR, T - 1);
+      graw[j] = *reinterpret_cast<const u32x4*>(
+          a.g + (((size_t)b * T + tt) * a.HV + hv) * K + (lane % GLPR) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < QNI; ++j) {
+      const int tt = min(n * C + 16 * I + QRPI * j + lane / QLPR, T - 1);
+      const size_t off = (((size_t)b * T + tt) * a.H + h) * K + (lane % QLPR) * (16 / sizeof(in_t));
+      qraw[j] = *reinterpret_cast<const u32x4*>(static_cast<const in_t*>(a.q) + off);
+      kraw[j] = *reinterpret_cast<const u32x4*>(static_cast<const in_t*>(a.k) + off);
+    }
+    bv = a.beta[((size_t)b * T + min(t, T - 1)) * a.HV + hv];
+    char* stg = sBig + (size_t)I * STG;
+    // g rows in, this lane's row out; then q and k rows over the same bytes
+    // (the LDS operations of one wave complete in order)
+#pragma unroll
+    for (int j = 0; j < GNI; ++j)
+      *reinterpret_cast<u32x4*>(stg + (GRPI * j + lane / GLPR) * GSR + (lane % GLPR) * 16) = graw[j];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      qr[kb] = P::load_raw8(qrow + 32 * kb + 8 * grp);
-      kr[kb] = P::load_raw8(krow + 32 * kb + 8 * grp);
-      glo[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 8 * grp);
-      ghi[kb] = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 8 * grp + 4);
+      const char* src = stg + r * GSR + (32 * kb + 8 * grp) * 4;
+      glo[kb] = *reinterpret_cast<const f32x4*>(src);
+      ghi[kb] = *reinterpret_cast<const f32x4*>(src + 16);
     }
-    bv = a.beta[((size_t)b * T + tt) * a.HV + hv];
+#pragma unroll
+    for (int j = 0; j < QNI; ++j) {
+      char* dst = stg + (QRPI * j + lane / QLPR) * QSR + (lane % QLPR) * 16;
+      *reinterpret_cast<u32x4*>(dst) = qraw[j];
+      *reinterpret_cast<u32x4*>(dst + 16 * QSR) = kraw[j];
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qr[kb] = P::load_raw8(reinterpret_cast<const in_t*>(stg + r * QSR) + 32 * kb + 8 * grp);
+      kr[kb] = P::load_raw8(reinterpret_cast<const in_t*>(stg + (16 + r) * QSR) + 32 * kb + 8 * grp);
+    }
   }
   if (!valid) bv = 0.f;
 
