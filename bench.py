@@ -263,10 +263,11 @@ def main():
     same = bool(torch.equal(o_ref, d["o"]))
 
     tm = traffic_model(w)
-    # the two stages of the path; the scan stage is up to three kernels (chain
-    # pass, segment combine, full pass) launched by one gdr_chunk_scan call
+    # the two stages of the path; the scan stage is up to two kernels (chain
+    # pass, then the full pass that also combines the segment transitions)
+    # launched by one gdr_chunk_scan call
     stages = {"chunk_prep": (prep_ms, tm["prep"], ("chunk_prep",)),
-              "state_scan": (scan_ms, tm["scan"], ("chunk_scan_kernel", "seg_combine_kernel"))}
+              "state_scan": (scan_ms, tm["scan"], ("chunk_scan_kernel",))}
     dom = max(stages, key=lambda k_: stages[k_][0])
     dom_ms, dom_bytes, dom_kernels = stages[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9

@@ -210,8 +210,6 @@ gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
     st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain>,
                 grid_for(BH * (r.nseg - 1), (K + V) / kScanBV), kScanWaves * 64, a, s);
     if (st != GDR_OK) return st;
-    st = launch(seg_combine_kernel<K, V, P>, grid_for(BH, V / kScanBV), kCombineWaves * 64, a, s);
-    if (st != GDR_OK) return st;
   }
   return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull>,
                 grid_for(BH * r.nseg, V / kScanBV), kScanWaves * 64, a, s);
@@ -259,7 +257,6 @@ ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
   a.B = r.B; a.T = r.T; a.H = r.H; a.HV = r.HV; a.N = r.N;
   a.scale = r.scale;
   a.seg_len = r.seg_len; a.nseg = r.nseg;
-  a.seg_state = reinterpret_cast<float*>(base + L.seg);
   a.phi = base + L.phi;
   a.eend = reinterpret_cast<float*>(base + L.eend);
   return a;

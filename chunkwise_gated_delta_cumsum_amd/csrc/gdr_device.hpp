@@ -21,7 +21,7 @@ namespace gdr {
 #ifdef GDR_WG_TIMES
 // Start and end of every workgroup on the chip-wide constant-rate clock
 // (profiling builds only): [kernel kind][block][2], kind 0 prep, 1 chain
-// pass, 2 combine, 3 full pass.
+// pass, 3 full pass.
 __device__ long long gdr_wg_times[4][32768][2];
 #define GDR_WGT(kind, which)                                                      \
   do {                                                                            \
@@ -41,6 +41,15 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;
+
+// Barrier for LDS traffic only: wait for this wave's LDS operations, then
+// the workgroup barrier.  No kernel here reads global memory that another
+// wave of its workgroup wrote, so outstanding global loads (a prefetch) and
+// stores (outputs draining to memory) stay in flight; __syncthreads would
+// wait for both.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ int kslot(int grp, int i) {
   return 4 * grp + (i & 3) + 16 * (i >> 2);
@@ -312,11 +321,11 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 //        are q exp(gamma) scale and k exp(gamma), one per value-head chunk;
 //        with one decay per row they are q and k themselves, converted to
 //        the workspace type, one per query-head chunk.
-//   seg, phi, eend : sequence segments (when more than one): start states
-//        [B*HV][nseg][K*V] fp32, transitions [B*HV][nseg-1][K][K] in the
-//        workspace type and zero-start end states [B*HV][nseg-1][K*V] fp32.
+//   phi, eend : sequence segments (when more than one): transitions
+//        [B*HV][nseg-1][K][K] in the workspace type (A-fragment order) and
+//        zero-start end states [B*HV][nseg-1][K*V] fp32 (tile order).
 struct WsLayout {
-  size_t wt, ah, rs, qh, kh, seg, phi, eend, total;
+  size_t wt, ah, rs, qh, kh, phi, eend, total;
 };
 
 __host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -332,9 +341,8 @@ __host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, i
   L.rs = off; off = ws_align(off + nchunks * 256 * sizeof(float));
   L.qh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
   L.kh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
-  L.seg = L.phi = L.eend = off;
+  L.phi = L.eend = off;
   if (nseg > 1) {
-    L.seg = off; off = ws_align(off + nheads * nseg * (size_t)K * V * sizeof(float));
     L.phi = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * K * elem);
     L.eend = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * V * sizeof(float));
   }

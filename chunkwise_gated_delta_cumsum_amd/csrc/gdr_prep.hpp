@@ -150,14 +150,14 @@ __device__ __forceinline__ void unit_lower_inverse(float* sL, float* sMT, int ti
       for (int i = 0; i < 16; ++i) Lb[i * LP + j] = x[i];
     }
   }
-  __syncthreads();   // every D_I is in sL
+  lds_barrier();   // every D_I is in sL
   switch (wave) {
     case 0: inverse_column<P, 0>(sL, sMT, x, r, grp); break;
     case 1: inverse_column<P, 1>(sL, sMT, x, r, grp); break;
     case 2: inverse_column<P, 2>(sL, sMT, x, r, grp); break;
     default: inverse_column<P, 3>(sL, sMT, x, r, grp); break;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ---- step 4a: W^ = M^-T diag(s) k -> A fragments of W^T --------------------
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     const float glast = __shfl(gv, 63, 64);
     sKs[lane] = bv * __expf(glast - gv);
   }
-  __syncthreads();
+  lds_barrier();
   GDR_PPROF(1);
 
   // ---- q and k for the scan, in its fragment order -------------------------
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
   }
 
-  __syncthreads();   // sL complete
+  lds_barrier();   // sL complete
   GDR_PPROF(2);
 
   if constexpr (DUMP) {

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
     }
   }
   if (grp == 0) sBeta[i] = bv;
-  __syncthreads();
+  lds_barrier();
   GDR_PPROF(1);
 
   // ---- per-channel tables (all threads) --------------------------------------
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
         }
     }
   }
-  __syncthreads();   // sKE and the tables are complete; the scratch is read
+  lds_barrier();   // sKE and the tables are complete; the scratch is read
   GDR_PPROF(2);
 
   // ---- off-diagonal tiles (J < I) ----------------------------------------------
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       store_ws4(sSK + i * SP + d0 + 4, wx + 4);
     }
   }
-  __syncthreads();   // sL and sSK complete; sKE and the tables are dead
+  lds_barrier();   // sL and sSK complete; sKE and the tables are dead
   GDR_PPROF(3);
 
   if constexpr (DUMP) {

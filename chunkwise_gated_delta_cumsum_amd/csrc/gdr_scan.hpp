@@ -10,14 +10,15 @@
 // fragments, so the row scales are 1.)
 //
 // The state update is affine in S: S_{n+1} = A_n S_n + B_n.  A sequence cut
-// into segments is therefore run in three passes:
+// into segments is therefore run in two passes:
 //   chain mode  : per (head, segment) the segment's transition Phi = prod A_n
 //                 (the scan run on an identity state with v = 0) and its
 //                 zero-start end state E (the scan run from S = 0), in
 //                 parallel over segments;
-//   combine     : S_{p+1} = Phi_p S_p + E_p, serial over segments;
 //   full mode   : the scan of every segment from its true start state,
-//                 writing o, in parallel over segments.
+//                 writing o, in parallel over segments; segment p first
+//                 runs the combine S_{q+1} = Phi_q S_q + E_q, q < p, itself
+//                 (combine_prefix).
 // With one segment only the full mode runs.
 //
 // Work split in a workgroup of NW = 4 waves (64 state columns, a "slab"):
@@ -69,15 +70,11 @@ struct ScanArgs {
   float scale;
   // segment p covers chunks [p * seg_len, min((p + 1) * seg_len, N))
   int seg_len, nseg;
-  float* seg_state;  // start states of the segments, tile order [BH][nseg][K*V]
   void* phi;         // transitions [BH][nseg-1], each K x K in A-fragment order
                      // [K/16 row tiles][K/32 k blocks][64 lanes][8], workspace type
   float* eend;       // zero-start end states, tile order [BH][nseg-1][K*V]
 };
 
-#ifdef GDR_COMBINE_PROFILE
-__device__ long long gdr_comb_prof[32 * 5 * 4];
-#endif
 #ifdef GDR_SCAN_PROFILE
 // clock marks of one chunk step, kept in registers and written out at the
 // end of the step (a store per mark would add waits of its own)
@@ -99,14 +96,7 @@ constexpr int kScanFull = 0;
 constexpr int kScanChain = 1;
 constexpr int kScanBV = 64;     // state columns per workgroup
 constexpr int kScanWaves = 4;
-constexpr int kCombineWaves = 4;
 
-// Barrier for LDS traffic only: wait for this wave's LDS operations, then
-// the workgroup barrier.  Outstanding global loads (the next chunk's
-// prefetch) stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Calls f(std::integral_constant<int, I>{}) for I = B .. E-1.
 template <int B, int E, class F>
@@ -153,6 +143,77 @@ __device__ __forceinline__ size_t state_tile(int sv, int dt, int ct) {
 template <int MODE>
 constexpr int scan_stage_bytes() {
   return MODE == kScanFull ? (kChunk / kScanWaves) * (kScanBV * 4 + 16) : 16;
+}
+
+// The start state of segment p from the chain pass's results:
+// S_{q+1} = Phi_q S_q + E_q for q = 0 .. p-1, from S_0 = the initial state
+// (in S on entry).  Each segment's workgroup runs its own prefix of this
+// short serial recurrence before its chunk loop, so no separate pass and no
+// round trip of the segment states through memory sits between the chain
+// and full passes.  Wave w owns state rows 16(SRT w + st) + 4grp + j (its
+// accumulator tiles); S crosses waves through LDS as B fragments, Phi_q
+// arrives as A fragments and E_q as accumulator tiles, both 16 contiguous
+// bytes per lane, the next step's loaded while this one computes.
+template <int K, int V, class P, int SRT>
+__device__ __forceinline__ void combine_prefix(const ScanArgs& a, typename P::frag_t* sS, int bh,
+                                               int p, int sv, int w, int lane,
+                                               f32x4 (&S)[SRT][kScanBV / 16]) {
+  using frag_t = typename P::frag_t;
+  using ws_t = typename P::ws_t;
+  constexpr int NCT = kScanBV / 16;
+  constexpr int KB = K / 32;
+  struct Ops {
+    frag_t ph[SRT][KB];     // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
+    f32x4 e[SRT][NCT];
+  };
+  const int nstep = a.nseg - 1;
+  auto load = [&](int q, Ops& op) {
+    const ws_t* ph = static_cast<const ws_t*>(a.phi) + ((size_t)bh * nstep + q) * K * K;
+    const float* e = a.eend + ((size_t)bh * nstep + q) * K * V;
+#pragma unroll
+    for (int st = 0; st < SRT; ++st) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        op.ph[st][kb] = frag_ws(ph + (((size_t)(SRT * w + st) * KB + kb) * 64 + lane) * 8);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        op.e[st][ct] = *reinterpret_cast<const f32x4*>(
+            e + state_tile<K>(sv, SRT * w + st, ct) + lane * 4);
+    }
+  };
+  auto step = [&](const Ops& cur) {
+#pragma unroll
+    for (int st = 0; st < SRT; ++st) {
+      const int tile = SRT * w + st;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int st = 0; st < SRT; ++st)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) S[st][ct] = cur.e[st][ct];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const frag_t fb = sS[(kb * NCT + ct) * 64 + lane];
+#pragma unroll
+        for (int st = 0; st < SRT; ++st) S[st][ct] = mma32(cur.ph[st][kb], fb, S[st][ct]);
+      }
+    lds_barrier();   // every wave has read sS before it is rewritten
+  };
+  Ops oa, ob;
+  load(0, oa);
+  int q = 0;
+  for (; q + 1 < p; q += 2) {
+    load(q + 1, ob);
+    step(oa);
+    if (q + 2 < p) load(q + 2, oa);
+    step(ob);
+  }
+  if (q < p) step(oa);
 }
 
 // One wave of a scan workgroup.  W (the wave index) and PHI (chain mode:
@@ -296,15 +357,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) S[st][ct] = zero4();
   if constexpr (FULL) {
-    if (p > 0) {
-      const float* src = a.seg_state + ((size_t)bh * a.nseg + p) * K * V;
-#pragma unroll
-      for (int st = 0; st < SRT; ++st)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          S[st][ct] = *reinterpret_cast<const f32x4*>(
-              src + state_tile<K>(sv, SRT * w + st, ct) + lane * 4);
-    } else if (a.s0) {
+    if (a.s0) {
 #pragma unroll
       for (int st = 0; st < SRT; ++st)
 #pragma unroll
@@ -315,6 +368,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
             S[st][ct][j] = a.s0[((size_t)bh * K + chan_of_row(d)) * V + v0 + 16 * ct + r];
           }
     }
+    if (p > 0) combine_prefix<K, V, P, SRT>(a, sS, bh, p, sv, w, lane, S);
   } else if constexpr (PHI) {
     // identity columns [64 sv, 64 sv + 64) of I_K
 #pragma unroll
@@ -595,141 +649,6 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   else if constexpr (!FULL)
     run(std::true_type{});
   GDR_WGT(FULL ? 3 : 1, 1);
-}
-
-// Combine pass: S_{p+1} = Phi_p S_p + E_p over the segments of one head,
-// one workgroup of four waves per (head, 64-column slab); wave w owns state
-// rows [K/4 w, K/4 (w+1)).  Phi_{p+1} and E_{p+1} are loaded while step p
-// computes.  Writes the start state of every segment p >= 1 in tile order.
-template <int K, int V, class P>
-__global__ __launch_bounds__(256) void seg_combine_kernel(ScanArgs a) {
-  using frag_t = typename P::frag_t;
-  using ws_t = typename P::ws_t;
-  constexpr int BV = kScanBV;
-  constexpr int NSLAB = V / BV;
-  constexpr int NCT = BV / 16;
-  constexpr int KT = K / 16;
-  constexpr int KB = K / 32;
-  constexpr int SRT = KT / kCombineWaves;
-
-  __shared__ frag_t sS[KB * NCT * 64];
-
-  int bh, sv;
-  if (!unit_block(a.B * a.HV, NSLAB, bh, sv)) return;
-  const int lane = threadIdx.x & 63, w = wave_id();
-  const int r = lane & 15, grp = lane >> 4;
-  const int v0 = sv * BV;
-  const int nstep = a.nseg - 1;
-  GDR_WGT(2, 0);
-
-  struct Ops {
-    frag_t ph[SRT][KB];     // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
-    f32x4 e[SRT][NCT];
-  };
-  // both operands are stored in the order the lanes consume them: 16
-  // contiguous bytes per lane
-  auto load = [&](int p, Ops& op) {
-    const ws_t* ph = static_cast<const ws_t*>(a.phi) + ((size_t)bh * nstep + p) * K * K;
-    const float* e = a.eend + ((size_t)bh * nstep + p) * K * V;
-#pragma unroll
-    for (int st = 0; st < SRT; ++st) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        op.ph[st][kb] = frag_ws(ph + (((size_t)(SRT * w + st) * KB + kb) * 64 + lane) * 8);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        op.e[st][ct] = *reinterpret_cast<const f32x4*>(
-            e + state_tile<K>(sv, SRT * w + st, ct) + lane * 4);
-    }
-  };
-
-  f32x4 S[SRT][NCT];
-#pragma unroll
-  for (int st = 0; st < SRT; ++st)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) S[st][ct] = zero4();
-  if (a.s0) {
-#pragma unroll
-    for (int st = 0; st < SRT; ++st)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 16 * (SRT * w + st) + 4 * grp + j;
-          S[st][ct][j] = a.s0[((size_t)bh * K + chan_of_row(d)) * V + v0 + 16 * ct + r];
-        }
-  }
-
-#ifdef GDR_COMBINE_PROFILE
-  long long cpt[5];
-#define GDR_CPROF(i) cpt[i] = clock64()
-#define GDR_CFLUSH(p)                                                              \
-  do {                                                                             \
-    if (bh == 0 && sv == 0 && lane == 0 && (p) < 32)                               \
-      for (int i_ = 0; i_ < 5; ++i_) gdr_comb_prof[((p) * 5 + i_) * 4 + w] = cpt[i_]; \
-  } while (0)
-#else
-#define GDR_CPROF(i) do {} while (0)
-#define GDR_CFLUSH(p) do {} while (0)
-#endif
-  auto step = [&](int p, const Ops& cur) {
-    GDR_CPROF(0);
-#pragma unroll
-    for (int st = 0; st < SRT; ++st) {
-      const int tile = SRT * w + st;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
-    }
-    lds_barrier();
-    GDR_CPROF(1);
-#pragma unroll
-    for (int st = 0; st < SRT; ++st)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) S[st][ct] = cur.e[st][ct];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const frag_t fb = sS[(kb * NCT + ct) * 64 + lane];
-#pragma unroll
-        for (int st = 0; st < SRT; ++st)
-          S[st][ct] = mma32(cur.ph[st][kb], fb, S[st][ct]);
-      }
-    GDR_CPROF(2);
-    float* dst = a.seg_state + ((size_t)bh * a.nseg + p + 1) * K * V;
-#pragma unroll
-    for (int st = 0; st < SRT; ++st)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        *reinterpret_cast<f32x4*>(dst + state_tile<K>(sv, SRT * w + st, ct) + lane * 4) =
-            S[st][ct];
-    GDR_CPROF(3);
-    lds_barrier();   // every wave has read sS before it is rewritten
-    GDR_CPROF(4);
-    GDR_CFLUSH(p);
-  };
-
-  // A ring of NB operand buffers, filled NB - 1 steps ahead (each step is
-  // short, so one step of lead does not cover the load latency); the loop is
-  // unrolled NB times so every buffer index is a compile-time constant.
-  constexpr int NB = 3;
-  Ops buf[NB];
-  static_for_scan<0, NB - 1>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
-    if (i < nstep) load(i, buf[i]);
-  });
-  for (int p0 = 0; p0 < nstep; p0 += NB) {
-    static_for_scan<0, NB>([&](auto bc) {
-      constexpr int bi = decltype(bc)::value;
-      const int p = p0 + bi;
-      if (p < nstep) {
-        if (p + NB - 1 < nstep) load(p + NB - 1, buf[(bi + NB - 1) % NB]);
-        step(p, buf[bi]);
-      }
-    });
-  }
-  GDR_WGT(2, 1);
 }
 
 }  // namespace gdr
