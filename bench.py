@@ -150,6 +150,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="sequence segments of the state scan (0: the library's choice)")
+    ap.add_argument("--slab", type=int, default=0, choices=(0, 32, 64),
+                    help="state columns per scan workgroup (0: the library's choice)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -187,7 +191,9 @@ def main():
                 g=to_dev(inp.g), beta=to_dev(inp.beta),
                 s0=None if inp.s0 is None else to_dev(inp.s0))
     prob = gdr.problem(w.B, w.T, w.H, w.HV, w.K, w.V, chunk=w.chunk,
-                       per_channel=w.per_channel, scale=inp.scale, dtype=w.dtype)
+                       per_channel=w.per_channel, scale=inp.scale, dtype=w.dtype,
+                       segments=args.segments, slab=args.slab)
+    knobs = dict(segments=args.segments, slab=args.slab)
     ws_bytes = gdr.workspace_size(prob)
     per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
     per_set += ws_bytes + w.B * w.T * w.HV * w.V * 4 + w.B * w.HV * w.K * w.V * 4
@@ -205,11 +211,11 @@ def main():
         if e0 is not None:
             e0.record()
         gdr.gdr_chunk_prep(d["q"], d["k"], d["g"], d["beta"], chunk=w.chunk, scale=inp.scale,
-                           V=w.V, workspace=d["ws"])
+                           V=w.V, workspace=d["ws"], **knobs)
         if e1 is not None:
             e1.record()
         gdr.gdr_chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["ws"], d["s0"],
-                           chunk=w.chunk, scale=inp.scale, out=(d["o"], d["sT"]))
+                           chunk=w.chunk, scale=inp.scale, out=(d["o"], d["sT"]), **knobs)
         if e2 is not None:
             e2.record()
 
@@ -249,16 +255,17 @@ def main():
         return a0.elapsed_time(a1) / KI
 
     prep_ms = stage_ms(lambda d: gdr.gdr_chunk_prep(d["q"], d["k"], d["g"], d["beta"], chunk=w.chunk,
-                                                   scale=inp.scale, V=w.V, workspace=d["ws"]))
+                                                   scale=inp.scale, V=w.V, workspace=d["ws"],
+                                                   **knobs))
     scan_ms = stage_ms(lambda d: gdr.gdr_chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                    d["ws"], d["s0"], chunk=w.chunk, scale=inp.scale,
-                                                   out=(d["o"], d["sT"])))
+                                                   out=(d["o"], d["sT"]), **knobs))
 
     # the path check: one more pass through the single-call entry point
     d = sets[0]
     o_ref = d["o"].clone()
     gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk=w.chunk,
-                      scale=inp.scale, workspace=d["ws"], out=(d["o"], d["sT"]))
+                      scale=inp.scale, workspace=d["ws"], out=(d["o"], d["sT"]), **knobs)
     torch.cuda.synchronize()
     same = bool(torch.equal(o_ref, d["o"]))
 
@@ -273,6 +280,7 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = measured_traffic(w, dom_kernels)
     nseg = gdr.scan_segments(prob)
+    slab = gdr.scan_slab(prob)
     ms_per_step = elapsed / K * 1e3
     tokens = w.B * w.T
     flops = algorithmic_flops(w)
@@ -301,7 +309,7 @@ def main():
                      "kernels": list(dom_kernels), "algorithmic_bytes": dom_bytes,
                      "kernel_ms": {"chunk_prep": prep_ms, "state_scan": scan_ms},
                      "step_stage_ms": {"chunk_prep": step_prep_ms, "state_scan": step_scan_ms},
-                     "scan_segments": nseg,
+                     "scan_segments": nseg, "scan_slab": slab,
                      "path_compulsory_bytes": tm["compulsory"],
                      "path_hbm_frac": tm["compulsory"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak},

@@ -23,7 +23,8 @@ STATUS_NAMES = {
     7: "GDR_ERR_DEVICE", 8: "GDR_ERR_HIP", 9: "GDR_ERR_ARG", 10: "GDR_ERR_ALIAS",
 }
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_prep",
-            "gdr_chunk_scan", "gdr_chunk_scan_segments", "gdr_status_string", "gdr_version")
+            "gdr_chunk_scan", "gdr_chunk_scan_segments", "gdr_chunk_scan_slab",
+            "gdr_status_string", "gdr_version")
 
 
 class GdrProblem(ctypes.Structure):
@@ -31,7 +32,7 @@ class GdrProblem(ctypes.Structure):
                 ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("g_per_channel", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32),
-                ("scan_segments", ctypes.c_int32)]
+                ("scan_segments", ctypes.c_int32), ("scan_slab", ctypes.c_int32)]
 
 
 class GdrError(RuntimeError):
@@ -67,6 +68,8 @@ def load():
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_chunk_scan_segments.argtypes = [P]
     lib.gdr_chunk_scan_segments.restype = ctypes.c_int
+    lib.gdr_chunk_scan_slab.argtypes = [P]
+    lib.gdr_chunk_scan_slab.restype = ctypes.c_int
     lib.gdr_version.argtypes = []
     lib.gdr_version.restype = ctypes.c_int
     _lib = lib
@@ -84,15 +87,20 @@ def check(status: int) -> None:
 
 def problem(B: int, T: int, H: int, HV: int, K: int, V: int, *, chunk: int = 64,
             per_channel: bool = False, scale: Optional[float] = None,
-            dtype: str = "bf16", segments: int = 0) -> GdrProblem:
+            dtype: str = "bf16", segments: int = 0, slab: int = 0) -> GdrProblem:
     return GdrProblem(B, T, H, HV, K, V, chunk, int(bool(per_channel)),
                       float(K ** -0.5 if scale is None else scale),
-                      {"fp32": GDR_F32, "bf16": GDR_BF16}[dtype], int(segments))
+                      {"fp32": GDR_F32, "bf16": GDR_BF16}[dtype], int(segments), int(slab))
 
 
 def scan_segments(prob: GdrProblem) -> int:
     """Segments the state scan uses for this problem (0: invalid problem)."""
     return int(load().gdr_chunk_scan_segments(ctypes.byref(prob)))
+
+
+def scan_slab(prob: GdrProblem) -> int:
+    """State columns per scan workgroup for this problem (0: invalid problem)."""
+    return int(load().gdr_chunk_scan_slab(ctypes.byref(prob)))
 
 
 def workspace_size(prob: GdrProblem) -> int:
@@ -103,7 +111,7 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _problem_from(q, k, v, g, beta, chunk, scale, segments=0) -> GdrProblem:
+def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0) -> GdrProblem:
     import torch
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
@@ -131,7 +139,8 @@ def _problem_from(q, k, v, g, beta, chunk, scale, segments=0) -> GdrProblem:
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
     return problem(B, T, H, HV, K, V, chunk=chunk, per_channel=per_channel, scale=scale,
-                   dtype="fp32" if q.dtype == torch.float32 else "bf16", segments=segments)
+                   dtype="fp32" if q.dtype == torch.float32 else "bf16", segments=segments,
+                   slab=slab)
 
 
 def _check_tensors(dev, **ts):
@@ -151,7 +160,7 @@ def _stream(dev) -> ctypes.c_void_p:
 
 def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
                   scale: Optional[float] = None, *, output_final_state: bool = True,
-                  workspace=None, out=None, segments: int = 0
+                  workspace=None, out=None, segments: int = 0, slab: int = 0
                   ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunkwise gated delta rule forward on the GPU.
 
@@ -161,13 +170,14 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     Returns (o [B, T, HV, V] float32, final_state [B, HV, K, V] float32 or None).
     ``workspace`` (uint8, at least workspace_size bytes) and ``out`` = (o, S)
     may be passed to avoid allocations.  ``segments`` > 0 asks for that many
-    sequence segments in the state scan (0: automatic).
+    sequence segments in the state scan (0: automatic); ``slab`` (32 or 64)
+    sets the state columns per scan workgroup (0: automatic).
     """
     import torch
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if initial_state is not None and (initial_state.dtype != torch.float32 or
@@ -193,7 +203,7 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
 
 def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None, *,
                    V: Optional[int] = None, inspect: bool = False,
-                   workspace=None, segments: int = 0
+                   workspace=None, segments: int = 0, slab: int = 0
                    ) -> Tuple["torch.Tensor", Dict[str, "torch.Tensor"]]:
     """Run the chunk-preparation stage alone.
 
@@ -204,7 +214,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, g=g, beta=beta)
-    prob = _problem_from(q, k, None, g, beta, chunk, scale, segments)
+    prob = _problem_from(q, k, None, g, beta, chunk, scale, segments, slab)
     if V is not None:
         prob.V = V
     nbytes = workspace_size(prob)
@@ -229,7 +239,8 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
 
 
 def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 64,
-                   scale: Optional[float] = None, *, out=None, segments: int = 0):
+                   scale: Optional[float] = None, *, out=None, segments: int = 0,
+                   slab: int = 0):
     """Run the state-scan stage on a workspace filled by gdr_chunk_prep.
 
     ``out`` = (o, final_state) reuses caller tensors (final_state may be None).
@@ -238,7 +249,7 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if out is not None:

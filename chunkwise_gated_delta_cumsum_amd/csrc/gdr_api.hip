@@ -25,6 +25,7 @@ struct Prob {
   float scale;
   size_t es;        // bytes per q/k/v element and per workspace fragment element
   int nseg, seg_len; // sequence segments of the state scan
+  int bv;            // state columns per scan workgroup (32 or 64)
 };
 
 // Number of sequence segments for the state scan.  One segment runs the
@@ -82,6 +83,8 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.scale = p->scale;
   r.es = r.f32 ? 4 : 2;
   if (p->scan_segments < 0) return GDR_ERR_ARG;
+  if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
+  r.bv = p->scan_slab != 0 ? p->scan_slab : 64;
   if (p->scan_segments == 0) {
     r.nseg = choose_segments(r.B * r.HV, r.N, r.K, r.V, r.seg_len);
   } else {
@@ -198,8 +201,8 @@ gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
                  : launch_prep_p<false, PolicyF16>(r, a, dump, s);
 }
 
-template <int K, int V, bool PERCH, class P>
-gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
+template <int K, int V, bool PERCH, class P, int BV>
+gdr_status launch_scan_kvb(const Prob& r, ScanArgs& a, hipStream_t s) {
   const size_t BH = (size_t)r.B * r.HV;
   auto grid_for = [](size_t units, int nslab) {
     // units rounded up to a multiple of the 8 XCDs; surplus workgroups exit
@@ -207,12 +210,18 @@ gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
   };
   gdr_status st;
   if (r.nseg > 1) {
-    st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain>,
-                grid_for(BH * (r.nseg - 1), (K + V) / kScanBV), kScanWaves * 64, a, s);
+    st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain, BV>,
+                grid_for(BH * (r.nseg - 1), (K + V) / BV), kScanWaves * 64, a, s);
     if (st != GDR_OK) return st;
   }
-  return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull>,
-                grid_for(BH * r.nseg, V / kScanBV), kScanWaves * 64, a, s);
+  return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, BV>,
+                grid_for(BH * r.nseg, V / BV), kScanWaves * 64, a, s);
+}
+
+template <int K, int V, bool PERCH, class P>
+gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
+  return r.bv == 32 ? launch_scan_kvb<K, V, PERCH, P, 32>(r, a, s)
+                    : launch_scan_kvb<K, V, PERCH, P, 64>(r, a, s);
 }
 
 template <bool PERCH, class P>
@@ -374,7 +383,7 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace NULL or smaller than gdr_chunk_fwd_workspace_size";
     case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE: the current HIP device is not gfx950";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP query or kernel launch failed";
-    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel 0 or 1, scan_segments >= 0";
+    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel 0 or 1, scan_segments >= 0, scan_slab 0, 32 or 64";
     case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: an output overlaps an input or another output";
     default: return "GDR_ERR_UNKNOWN: unknown status value";
   }
@@ -384,6 +393,12 @@ int gdr_chunk_scan_segments(const gdr_problem* p) {
   Prob r;
   if (validate(p, &r) != GDR_OK) return 0;
   return r.nseg;
+}
+
+int gdr_chunk_scan_slab(const gdr_problem* p) {
+  Prob r;
+  if (validate(p, &r) != GDR_OK) return 0;
+  return r.bv;
 }
 
 int gdr_version(void) { return 100; }

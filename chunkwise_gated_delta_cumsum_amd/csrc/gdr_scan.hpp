@@ -21,7 +21,8 @@
 //                 (combine_prefix).
 // With one segment only the full mode runs.
 //
-// Work split in a workgroup of NW = 4 waves (64 state columns, a "slab"):
+// Work split in a workgroup of NW = 4 waves (BV = 32 or 64 state columns, a
+// "slab"):
 // wave w owns chunk rows [16w, 16w+16) of Y, Z and o and state rows
 // [K/4 w, K/4 (w+1)).  Every A-operand fragment (k, q, W^T and A^ rows)
 // belongs to exactly one wave, which loads it straight into registers.  The
@@ -94,7 +95,7 @@ __device__ long long gdr_scan_prof[64 * 16 * 4];
 
 constexpr int kScanFull = 0;
 constexpr int kScanChain = 1;
-constexpr int kScanBV = 64;     // state columns per workgroup
+constexpr int kScanBV = 64;     // widest slab: state columns per workgroup
 constexpr int kScanWaves = 4;
 
 
@@ -134,15 +135,15 @@ __device__ __forceinline__ bool unit_block(int nunits, int nslab, int& unit, int
 // Offset (floats) of accumulator tile (state row tile dt, column tile ct) of
 // slab sv inside one K x V state kept in tile order:
 // [slab][row tile][column tile][64 lanes][4].
-template <int K>
+template <int K, int BV>
 __device__ __forceinline__ size_t state_tile(int sv, int dt, int ct) {
-  return (((size_t)sv * (K / 16) + dt) * (kScanBV / 16) + ct) * 256;
+  return (((size_t)sv * (K / 16) + dt) * (BV / 16) + ct) * 256;
 }
 
 // Bytes of one wave's staging area for its fp32 o rows (full mode only).
-template <int MODE>
+template <int MODE, int BV>
 constexpr int scan_stage_bytes() {
-  return MODE == kScanFull ? (kChunk / kScanWaves) * (kScanBV * 4 + 16) : 16;
+  return MODE == kScanFull ? (kChunk / kScanWaves) * (BV * 4 + 16) : 16;
 }
 
 // The start state of segment p from the chain pass's results:
@@ -154,13 +155,13 @@ constexpr int scan_stage_bytes() {
 // accumulator tiles); S crosses waves through LDS as B fragments, Phi_q
 // arrives as A fragments and E_q as accumulator tiles, both 16 contiguous
 // bytes per lane, the next step's loaded while this one computes.
-template <int K, int V, class P, int SRT>
+template <int K, int V, class P, int SRT, int BV>
 __device__ __forceinline__ void combine_prefix(const ScanArgs& a, typename P::frag_t* sS, int bh,
                                                int p, int sv, int w, int lane,
-                                               f32x4 (&S)[SRT][kScanBV / 16]) {
+                                               f32x4 (&S)[SRT][BV / 16]) {
   using frag_t = typename P::frag_t;
   using ws_t = typename P::ws_t;
-  constexpr int NCT = kScanBV / 16;
+  constexpr int NCT = BV / 16;
   constexpr int KB = K / 32;
   struct Ops {
     frag_t ph[SRT][KB];     // Phi rows 16(SRT w + st) + r, columns 32kb + kslot(grp, .)
@@ -178,7 +179,7 @@ __device__ __forceinline__ void combine_prefix(const ScanArgs& a, typename P::fr
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
         op.e[st][ct] = *reinterpret_cast<const f32x4*>(
-            e + state_tile<K>(sv, SRT * w + st, ct) + lane * 4);
+            e + state_tile<K, BV>(sv, SRT * w + st, ct) + lane * 4);
     }
   };
   auto step = [&](const Ops& cur) {
@@ -219,7 +220,7 @@ __device__ __forceinline__ void combine_prefix(const ScanArgs& a, typename P::fr
 // One wave of a scan workgroup.  W (the wave index) and PHI (chain mode:
 // transition slab, identity start and no v) are template arguments so that
 // every choice between waves and slab kinds folds at compile time.
-template <int K, int V, bool PERCH, class P, int MODE, int NW, int W, bool PHI>
+template <int K, int V, bool PERCH, class P, int MODE, int BV, int NW, int W, bool PHI>
 __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t* sS,
                                           typename P::frag_t* sZ, typename P::in_t* sVw,
                                           unsigned char* stg, int unit, int sv) {
@@ -228,7 +229,6 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   using ws_t = typename P::ws_t;
   constexpr bool FULL = MODE == kScanFull;
   constexpr int C = kChunk;
-  constexpr int BV = kScanBV;
   constexpr int NCT = BV / 16;     // column tiles
   constexpr int KT = K / 16;       // state row tiles
   constexpr int KB = K / 32;       // 32-wide k blocks over K
@@ -368,7 +368,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
             S[st][ct][j] = a.s0[((size_t)bh * K + chan_of_row(d)) * V + v0 + 16 * ct + r];
           }
     }
-    if (p > 0) combine_prefix<K, V, P, SRT>(a, sS, bh, p, sv, w, lane, S);
+    if (p > 0) combine_prefix<K, V, P, SRT, BV>(a, sS, bh, p, sv, w, lane, S);
   } else if constexpr (PHI) {
     // identity columns [64 sv, 64 sv + 64) of I_K
 #pragma unroll
@@ -608,26 +608,26 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     for (int st = 0; st < SRT; ++st)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        *reinterpret_cast<f32x4*>(dst + state_tile<K>(sv - K / BV, SRT * w + st, ct) +
+        *reinterpret_cast<f32x4*>(dst + state_tile<K, BV>(sv - K / BV, SRT * w + st, ct) +
                                   lane * 4) = S[st][ct];
   }
 }
 
-template <int K, int V, bool PERCH, class P, int MODE>
+template <int K, int V, bool PERCH, class P, int MODE, int BV>
 __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
   constexpr int NW = kScanWaves;
   constexpr bool FULL = MODE == kScanFull;
-  constexpr int NSLAB = FULL ? V / kScanBV : (K + V) / kScanBV;
-  constexpr int NCT = kScanBV / 16;
+  constexpr int NSLAB = FULL ? V / BV : (K + V) / BV;
+  constexpr int NCT = BV / 16;
   constexpr int KB = K / 32;
   constexpr int VVEC = 16 / (int)sizeof(in_t);
-  constexpr int VP = kScanBV + VVEC;
+  constexpr int VP = BV + VVEC;
   __shared__ frag_t sS[KB * NCT * 64];                // B fragments of S
   __shared__ frag_t sZ[2 * NCT * 64];                 // B fragments of Z
   __shared__ __attribute__((aligned(16))) in_t sV[NW][(64 / NW) * VP];
-  __shared__ __attribute__((aligned(16))) unsigned char sStg[NW][scan_stage_bytes<MODE>()];
+  __shared__ __attribute__((aligned(16))) unsigned char sStg[NW][scan_stage_bytes<MODE, BV>()];
 
   const int nsegu = FULL ? a.nseg : a.nseg - 1;       // segments handled by this pass
   int unit, sv;
@@ -636,15 +636,15 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   GDR_WGT(FULL ? 3 : 1, 0);
   auto run = [&](auto phi) {
     constexpr bool PHI = decltype(phi)::value;
-    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, NW, 0, PHI>(a, sS, sZ, sV[0], sStg[0], unit, sv);
+    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, BV, NW, 0, PHI>(a, sS, sZ, sV[0], sStg[0], unit, sv);
     if constexpr (NW > 1)
-      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, NW, 1, PHI>(a, sS, sZ, sV[1], sStg[1], unit, sv);
+      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, BV, NW, 1, PHI>(a, sS, sZ, sV[1], sStg[1], unit, sv);
     if constexpr (NW > 2) {
-      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, NW, 2, PHI>(a, sS, sZ, sV[2], sStg[2], unit, sv);
-      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, NW, 3, PHI>(a, sS, sZ, sV[3], sStg[3], unit, sv);
+      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, BV, NW, 2, PHI>(a, sS, sZ, sV[2], sStg[2], unit, sv);
+      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, BV, NW, 3, PHI>(a, sS, sZ, sV[3], sStg[3], unit, sv);
     }
   };
-  if (FULL || sv >= K / kScanBV)
+  if (FULL || sv >= K / BV)
     run(std::false_type{});
   else if constexpr (!FULL)
     run(std::true_type{});

@@ -68,7 +68,8 @@ typedef enum gdr_status {
   GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query */
   GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
   GDR_ERR_HIP = 8,         /* a HIP query or kernel launch failed */
-  GDR_ERR_ARG = 9,         /* scale not finite, or g_per_channel not 0/1 */
+  GDR_ERR_ARG = 9,         /* scale not finite, g_per_channel not 0/1,
+                              scan_segments < 0 or scan_slab not 0, 32 or 64 */
   GDR_ERR_ALIAS = 10       /* an output overlaps an input or the other output
                               (final_state == initial_state exactly is allowed) */
 } gdr_status;
@@ -85,6 +86,10 @@ typedef struct gdr_problem {
                                 automatically (gdr_chunk_scan_segments), n > 0
                                 asks for n (rounded so that every segment holds
                                 the same number of chunks, at most one per chunk) */
+  int32_t scan_slab;         /* state columns per state-scan workgroup: 0 chooses
+                                automatically (gdr_chunk_scan_slab), or 32 or 64;
+                                any width gives the same result up to rounding
+                                order, it only moves work between workgroups */
 } gdr_problem;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when
@@ -145,6 +150,13 @@ gdr_status gdr_chunk_scan(const gdr_problem* p,
  * automatic choice comes from a cost model of the MI355X (256 compute
  * units) and the problem sizes only. */
 int gdr_chunk_scan_segments(const gdr_problem* p);
+
+/* State columns per state-scan workgroup for problem `p` (32 or 64), or 0
+ * when `p` fails validation.  Narrow slabs spread each scan over more
+ * workgroups, which shortens the serial chunk step when few scans run; wide
+ * slabs read each chunk's operands fewer times.  The automatic choice uses
+ * the problem sizes only. */
+int gdr_chunk_scan_slab(const gdr_problem* p);
 
 /* Static, never-NULL text for any status value (unknown values included). */
 const char* gdr_status_string(int status);

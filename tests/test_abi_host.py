@@ -175,3 +175,15 @@ def test_scan_segment_query(lib):
     assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"
     # more segments need more workspace (transitions and states)
     assert gdr.workspace_size(base(T=4096, segments=8)) > gdr.workspace_size(base(T=4096, segments=1))
+
+
+def test_scan_slab_query(lib):
+    assert gdr.scan_slab(base(T=4096, H=12, HV=12)) in (32, 64)
+    for want in (32, 64):
+        p = base(T=4096, H=12, HV=12, slab=want)
+        assert gdr.scan_slab(p) == want
+        assert gdr.workspace_size(p) > 0
+    for bad_slab in (-1, 16, 48, 128):
+        bad = base(slab=bad_slab)
+        assert gdr.scan_slab(bad) == 0
+        assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"

@@ -265,13 +265,32 @@ SEG_CASES = [
 
 @pytest.mark.parametrize("w,segs", SEG_CASES, ids=[c[0].name for c in SEG_CASES])
 def test_scan_segments(gpu_lib, w, segs):
-    """The segmented scan (transitions, combine, rerun) matches the oracle."""
+    """The segmented scan (transitions, combine, rerun) matches the oracle, with
+    32- and 64-column state slabs per workgroup."""
     inp = make_inputs(w)
     ro, rs = oracle_full(inp)
     for nseg in segs:
-        prob = gpu_lib.problem(w.B, w.T, w.H, w.HV, w.K, w.V, per_channel=w.per_channel,
-                               dtype=w.dtype, segments=nseg)
-        used = gpu_lib.scan_segments(prob)
-        assert 1 <= used <= nseg
-        o, s = run_gpu(gpu_lib, inp, segments=nseg)
-        check(o, s, ro, rs, w.dtype, f"{w.name} segments={nseg}->{used}")
+        for slab in (32, 64):
+            prob = gpu_lib.problem(w.B, w.T, w.H, w.HV, w.K, w.V, per_channel=w.per_channel,
+                                   dtype=w.dtype, segments=nseg, slab=slab)
+            used = gpu_lib.scan_segments(prob)
+            assert 1 <= used <= nseg
+            assert gpu_lib.scan_slab(prob) == slab
+            o, s = run_gpu(gpu_lib, inp, segments=nseg, slab=slab)
+            check(o, s, ro, rs, w.dtype, f"{w.name} segments={nseg}->{used} slab={slab}")
+
+
+SLAB_SHAPES = [(64, 64), (64, 128), (128, 64)]
+
+
+@pytest.mark.parametrize("KV", SLAB_SHAPES, ids=[f"K{k}V{v}" for k, v in SLAB_SHAPES])
+def test_slab_widths_small_heads(gpu_lib, KV):
+    """Both slab widths at K, V = 64 (fewer slabs per head), segmented and not."""
+    K, V = KV
+    w = WORKLOADS[3].with_(B=1, T=450, K=K, V=V)
+    inp = make_inputs(w)
+    ro, rs = oracle_full(inp)
+    for nseg in (1, 3):
+        for slab in (32, 64):
+            o, s = run_gpu(gpu_lib, inp, segments=nseg, slab=slab)
+            check(o, s, ro, rs, w.dtype, f"K={K} V={V} segments={nseg} slab={slab}")
