@@ -127,6 +127,95 @@ def cpu_baseline(inp, budget_s):
             "sample": sample}
 
 
+def decode_traffic(w):
+    """Algorithmic bytes of one decode step: the state read and written once,
+    the token's q, k (per q/k head), v, g, beta read and o written."""
+    es = 4 if w.dtype == "fp32" else 2
+    heads = w.B * w.HV
+    state = heads * w.K * w.V * 4
+    vec = (2 * w.B * w.H * w.K * es + heads * w.V * es
+           + heads * (w.K if w.per_channel else 1) * 4 + heads * 4 + heads * w.V * 4)
+    return 2 * state + vec
+
+
+def bench_decode(args, w, inp):
+    """Decode steps (one token per sequence, state updated in place), each
+    one launch of the decode kernel over the whole batch."""
+    import numpy as np
+    import torch
+    import chunkwise_gated_delta_cumsum_amd as gdr
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    tok = dict(q=to_dev(inp.q_dev[:, 0]), k=to_dev(inp.k_dev[:, 0]), v=to_dev(inp.v_dev[:, 0]),
+               g=to_dev(inp.g[:, 0]), beta=to_dev(inp.beta[:, 0]))
+    s0 = to_dev(inp.s0)
+    per_set = 2 * s0.numel() * 4
+    nsets = args.sets or max(2, -(-(640 << 20) // per_set))
+    sets = []
+    for i in range(nsets):
+        d = {k_: (t if i == 0 else t.clone()) for k_, t in tok.items()}
+        d["s"] = s0.clone()
+        d["o"] = torch.empty((w.B, w.HV, w.V), dtype=torch.float32, device="cuda")
+        sets.append(d)
+
+    def step(d):
+        gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s"], scale=inp.scale,
+                            out=(d["o"], d["s"]))
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # the kernel's launch duration: back-to-back launches between one pair of
+    # events on the launch stream
+    KI = max(K, 20)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for i in range(KI):
+        step(sets[i % nsets])
+    a1.record()
+    torch.cuda.synchronize()
+    kernel_ms = a0.elapsed_time(a1) / KI
+    nbytes = decode_traffic(w)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    ms_per_step = elapsed / K * 1e3
+    rec = {
+        "metric": "tokens/sec of gated-delta-rule decode step at 1 GPU; % HBM roofline",
+        "value": w.B / (elapsed / K),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": 1, "H": w.H, "HV": w.HV, "K": w.K,
+                   "V": w.V, "decay": "per-channel" if w.per_channel else "scalar",
+                   "inputs": w.dtype, "state": "fp32, updated in place",
+                   "rotating_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w, ("decode_step_kernel",)),
+                     "kernel": "decode_step", "kernels": ["decode_step_kernel"],
+                     "algorithmic_bytes": nbytes, "kernel_ms": {"decode_step": kernel_ms}},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(mib, reps):
     """Plain device copy of known size, for scaling rocprof FETCH/WRITE_SIZE."""
     import torch
@@ -179,6 +268,9 @@ def main():
     gdr.load()
     w = workload(args.workload)
     inp = make_inputs(w)
+    if w.T == 1:
+        bench_decode(args, w, inp)
+        return
     dev = torch.device("cuda", 0)
 
     def to_dev(a):

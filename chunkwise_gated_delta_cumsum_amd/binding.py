@@ -24,7 +24,7 @@ STATUS_NAMES = {
 }
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_prep",
             "gdr_chunk_scan", "gdr_chunk_scan_segments", "gdr_chunk_scan_slab",
-            "gdr_status_string", "gdr_version")
+            "gdr_decode_step", "gdr_status_string", "gdr_version")
 
 
 class GdrProblem(ctypes.Structure):
@@ -69,6 +69,8 @@ def load():
     lib.gdr_chunk_scan_segments.argtypes = [P]
     lib.gdr_chunk_scan_segments.restype = ctypes.c_int
     lib.gdr_chunk_scan_slab.argtypes = [P]
+    lib.gdr_decode_step.argtypes = [P] + [vp] * 8 + [vp]
+    lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_chunk_scan_slab.restype = ctypes.c_int
     lib.gdr_version.argtypes = []
     lib.gdr_version.restype = ctypes.c_int
@@ -259,5 +261,59 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
         s = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     st = lib.gdr_chunk_scan(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(initial_state),
                             _ptr(o), _ptr(s), _ptr(workspace), workspace.numel(), _stream(dev))
+    check(st)
+    return o, s
+
+
+def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None, *,
+                    out=None, inplace: bool = False
+                    ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """One decode step (one token per sequence) on the GPU.
+
+    q, k: [B, H, K]; v: [B, HV, V] (float32 or bfloat16, one dtype);
+    g: [B, HV] or [B, HV, K] float32 log-decay; beta: [B, HV] float32;
+    state: [B, HV, K, V] float32 or None (zero state).  scale defaults to
+    K**-0.5.  Returns (o [B, HV, V] float32, new state [B, HV, K, V] float32).
+    With ``inplace`` the new state overwrites ``state``; ``out`` = (o, S) may
+    be passed to avoid allocations.
+    """
+    import torch
+    lib = load()
+    dev = q.device
+    _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, state=state)
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 3 or k.shape != q.shape:
+        raise ValueError(f"q and k must be [B, H, K] of one shape: {tuple(q.shape)}, {tuple(k.shape)}")
+    B, H, K = q.shape
+    if v.dim() != 3 or v.shape[0] != B:
+        raise ValueError(f"v must be [B, HV, V], got {tuple(v.shape)}")
+    HV, V = v.shape[1], v.shape[2]
+    if g.shape == (B, HV):
+        per_channel = False
+    elif g.shape == (B, HV, K):
+        per_channel = True
+    else:
+        raise ValueError(f"g must be [B, HV] or [B, HV, K], got {tuple(g.shape)}")
+    if beta.shape != (B, HV):
+        raise ValueError(f"beta must be [B, HV], got {tuple(beta.shape)}")
+    for name, t in (("g", g), ("beta", beta)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if state is not None and (state.dtype != torch.float32 or state.shape != (B, HV, K, V)):
+        raise ValueError("state must be float32 [B, HV, K, V]")
+    if inplace and state is None:
+        raise ValueError("inplace needs a state")
+    prob = problem(B, 1, H, HV, K, V, per_channel=per_channel, scale=scale,
+                   dtype="fp32" if q.dtype == torch.float32 else "bf16")
+    if out is not None:
+        o, s = out
+    else:
+        o = torch.empty((B, HV, V), dtype=torch.float32, device=dev)
+        s = state if inplace else torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
+    st = lib.gdr_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                             _ptr(beta), _ptr(state), _ptr(s), _ptr(o), _stream(dev))
     check(st)
     return o, s

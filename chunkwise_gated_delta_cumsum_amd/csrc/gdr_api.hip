@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "gdr.h"
+#include "gdr_decode.hpp"
 #include "gdr_device.hpp"
 #include "gdr_prep_kda.hpp"
 #include "gdr_scan.hpp"
@@ -277,9 +278,67 @@ gdr_status check_ws(const Prob& r, const void* ws, size_t ws_bytes) {
   return GDR_OK;
 }
 
+template <int K, int V, bool PERCH>
+gdr_status launch_decode_kv(bool f32, DecodeArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)a.B * a.HV);
+  if (f32) return launch(decode_step_kernel<K, V, PERCH, float>, grid, 256, a, s);
+  return launch(decode_step_kernel<K, V, PERCH, uint16_t>, grid, 256, a, s);
+}
+
+template <bool PERCH>
+gdr_status launch_decode_p(int K, int V, bool f32, DecodeArgs& a, hipStream_t s) {
+  if (K == 64)
+    return V == 64 ? launch_decode_kv<64, 64, PERCH>(f32, a, s)
+                   : launch_decode_kv<64, 128, PERCH>(f32, a, s);
+  return V == 64 ? launch_decode_kv<128, 64, PERCH>(f32, a, s)
+                 : launch_decode_kv<128, 128, PERCH>(f32, a, s);
+}
+
 }  // namespace
 
 extern "C" {
+
+gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* state_in,
+                           float* state_out, float* o, void* stream) {
+  if (!p) return GDR_ERR_NULL;
+  if (p->B < 1 || p->T != 1 || p->H < 1 || p->HV < 1 || p->K < 1 || p->V < 1 ||
+      p->HV % p->H != 0)
+    return GDR_ERR_SHAPE;
+  if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
+  if ((p->g_per_channel != 0 && p->g_per_channel != 1) || !std::isfinite(p->scale))
+    return GDR_ERR_ARG;
+  if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
+  if ((uint64_t)p->B * p->HV > 0x7fffffffull) return GDR_ERR_SHAPE;
+  if (!q || !k || !v || !g || !beta || !state_out || !o) return GDR_ERR_NULL;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
+                          (const void*)beta, (const void*)state_in, (const void*)state_out,
+                          (const void*)o})
+    if (ptr && !aligned16(ptr)) return GDR_ERR_ALIGN;
+  const size_t es = p->qkv_dtype == GDR_F32 ? 4 : 2;
+  const size_t heads = (size_t)p->B * p->HV;
+  const Span sq = {q, (size_t)p->B * p->H * p->K * es}, sk = {k, sq.n};
+  const Span sv = {v, heads * p->V * es};
+  const Span sg = {g, heads * (p->g_per_channel ? p->K : 1) * sizeof(float)};
+  const Span sb = {beta, heads * sizeof(float)};
+  const Span si = {state_in, heads * p->K * p->V * sizeof(float)};
+  const Span so = {state_out, si.n};
+  const Span sO = {o, heads * p->V * sizeof(float)};
+  if (out_overlaps(sO, {sq, sk, sv, sg, sb, si, so})) return GDR_ERR_ALIAS;
+  if (out_overlaps(so, {sq, sk, sv, sg, sb})) return GDR_ERR_ALIAS;
+  if (state_in && state_in != state_out && overlap(si, so)) return GDR_ERR_ALIAS;
+  gdr_status st = check_device();
+  if (st != GDR_OK) return st;
+  DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.s_in = state_in; a.s_out = state_out; a.o = o;
+  a.B = p->B; a.H = p->H; a.HV = p->HV;
+  a.scale = p->scale;
+  const bool f32 = p->qkv_dtype == GDR_F32;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  return p->g_per_channel ? launch_decode_p<true>(p->K, p->V, f32, a, hs)
+                          : launch_decode_p<false>(p->K, p->V, f32, a, hs);
+}
 
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
   Prob r;

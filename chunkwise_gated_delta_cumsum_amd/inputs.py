@@ -28,7 +28,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "Inputs", "make_inputs", "workload",
+__all__ = ["Workload", "WORKLOADS", "DECODE_WORKLOADS", "Inputs", "make_inputs", "workload",
            "bf16_round", "bf16_bits_to_f64"]
 
 
@@ -79,10 +79,22 @@ WORKLOADS = (
 )
 
 
+# Decode batches: one token per sequence (T = 1) against a state carried
+# over from earlier tokens, drawn as 0.1 N(0, 1) like the grouped-head
+# workload's initial state.  The shapes are the grouped-head and the
+# per-channel workloads' heads at serving batch sizes.
+DECODE_WORKLOADS = (
+    Workload("decode_bf16_B64_H16_HV32_D128", B=64, T=1, H=16, HV=32, K=128, V=128,
+             dtype="bf16", g_mu=3.0, s0_std=0.1, seed=47),
+    Workload("decode_kda_bf16_B32_H16_D128", B=32, T=1, H=16, HV=16, K=128, V=128,
+             per_channel=True, dtype="bf16", g_mu=4.0, s0_std=0.1, seed=48),
+)
+
+
 def workload(i_or_name) -> Workload:
     if isinstance(i_or_name, int):
         return WORKLOADS[i_or_name]
-    for w in WORKLOADS:
+    for w in WORKLOADS + DECODE_WORKLOADS:
         if w.name == i_or_name:
             return w
     raise KeyError(i_or_name)

@@ -145,6 +145,31 @@ gdr_status gdr_chunk_scan(const gdr_problem* p,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* One decode step (the recurrent form of the same rule, for serving one
+ * token at a time): for every batch b and value head hv, with
+ * d = exp(g) (one value, or one per key channel when g_per_channel = 1),
+ *     u  = v - (diag(d) S)^T k
+ *     S' = diag(d) S + beta k u^T
+ *     o  = scale S'^T q
+ * (sec-03 notes: the naive recurrence the chunkwise form equals; "Chunkwise
+ * parallel algorithms" page, section 2.1: the delta rule).  The problem
+ * takes T = 1 (GDR_ERR_SHAPE otherwise); chunk, scan_segments and scan_slab
+ * are ignored.  Layouts are those of gdr_chunk_fwd with the token axis of
+ * extent 1:
+ *   q, k  [B, H, K]  qkv_dtype        v  [B, HV, V]  qkv_dtype
+ *   g     [B, HV] or [B, HV, K] fp32  beta [B, HV]   fp32
+ *   state_in  [B, HV, K, V] fp32, or NULL for a zero state
+ *   state_out [B, HV, K, V] fp32 (required); state_out == state_in updates
+ *             the state in place (a partial overlap is GDR_ERR_ALIAS)
+ *   o     [B, HV, V] fp32
+ * No workspace.  Validation, errors and streams as for gdr_chunk_fwd.  The
+ * kernel reads and writes the state once: it is bound by HBM bandwidth. */
+gdr_status gdr_decode_step(const gdr_problem* p,
+                           const void* q, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           const float* state_in, float* state_out, float* o,
+                           void* stream);
+
 /* Number of sequence segments the state scan of problem `p` uses (1: one
  * serial scan over all chunks), or 0 when `p` fails validation.  The
  * automatic choice comes from a cost model of the MI355X (256 compute

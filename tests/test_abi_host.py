@@ -187,3 +187,35 @@ def test_scan_slab_query(lib):
         bad = base(slab=bad_slab)
         assert gdr.scan_slab(bad) == 0
         assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"
+
+
+def call_decode(lib, prob, q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, s_in=6 * A,
+                s_out=7 * A, o=8 * A):
+    ref = None if prob is None else ctypes.byref(prob)
+    return lib.gdr_decode_step(ref, q, k, v, g, beta, s_in, s_out, o, None)
+
+
+def test_decode_validation(lib):
+    """Each bad argument of gdr_decode_step gets its status before any HIP call."""
+    name = lambda st: binding.STATUS_NAMES[st]
+    ok = base(T=1, B=2, H=2, HV=4)
+    assert name(call_decode(lib, None)) == "GDR_ERR_NULL"
+    assert name(call_decode(lib, base(T=2))) == "GDR_ERR_SHAPE"          # one token only
+    assert name(call_decode(lib, base(T=1, H=3, HV=4))) == "GDR_ERR_SHAPE"
+    assert name(call_decode(lib, base(T=1, K=96))) == "GDR_ERR_UNSUPPORTED"
+    bad_dtype = base(T=1)
+    bad_dtype.qkv_dtype = 7
+    assert name(call_decode(lib, bad_dtype)) == "GDR_ERR_DTYPE"
+    bad_scale = base(T=1, scale=float("nan"))
+    assert name(call_decode(lib, bad_scale)) == "GDR_ERR_ARG"
+    for kw in ("q", "k", "v", "g", "beta", "s_out", "o"):
+        assert name(call_decode(lib, ok, **{kw: None})) == "GDR_ERR_NULL", kw
+    assert name(call_decode(lib, ok, q=A + 4)) == "GDR_ERR_ALIGN"
+    # o must not overlap anything; the new state must not overlap the inputs;
+    # the state may be updated exactly in place but not with a partial overlap
+    assert name(call_decode(lib, ok, o=7 * A)) == "GDR_ERR_ALIAS"
+    assert name(call_decode(lib, ok, s_out=A)) == "GDR_ERR_ALIAS"
+    assert name(call_decode(lib, ok, s_out=6 * A + 1024)) == "GDR_ERR_ALIAS"
+    # the chunk settings do not apply to a single token
+    odd = base(T=1, B=2, H=2, HV=4, chunk=32, segments=5)
+    assert name(call_decode(lib, odd, q=A + 4)) == "GDR_ERR_ALIGN"
