@@ -164,7 +164,7 @@ def bench_decode(args, w, inp):
 
     def step(d):
         gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s"], scale=inp.scale,
-                            out=(d["o"], d["s"]))
+                            out=(d["o"], d["s"]), slab=args.slab)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -204,6 +204,7 @@ def bench_decode(args, w, inp):
         "config": {"workload": w.name, "B": w.B, "T": 1, "H": w.H, "HV": w.HV, "K": w.K,
                    "V": w.V, "decay": "per-channel" if w.per_channel else "scalar",
                    "inputs": w.dtype, "state": "fp32, updated in place",
+                   "columns_per_workgroup": args.slab or "auto",
                    "rotating_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -241,8 +242,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0,
                     help="sequence segments of the state scan (0: the library's choice)")
-    ap.add_argument("--slab", type=int, default=0, choices=(0, 32, 64),
-                    help="state columns per scan workgroup (0: the library's choice)")
+    ap.add_argument("--slab", type=int, default=0, choices=(0, 32, 64, 128),
+                    help="state columns per scan (32, 64) or decode (32, 64, 128) "
+                         "workgroup (0: the library's choice)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()

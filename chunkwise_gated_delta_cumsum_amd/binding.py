@@ -266,7 +266,7 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
 
 
 def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None, *,
-                    out=None, inplace: bool = False
+                    out=None, inplace: bool = False, slab: int = 0
                     ) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """One decode step (one token per sequence) on the GPU.
 
@@ -275,7 +275,8 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     state: [B, HV, K, V] float32 or None (zero state).  scale defaults to
     K**-0.5.  Returns (o [B, HV, V] float32, new state [B, HV, K, V] float32).
     With ``inplace`` the new state overwrites ``state``; ``out`` = (o, S) may
-    be passed to avoid allocations.
+    be passed to avoid allocations.  ``slab`` (32, 64 or 128) sets the state
+    columns per workgroup (0: automatic).
     """
     import torch
     lib = load()
@@ -307,7 +308,7 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     if inplace and state is None:
         raise ValueError("inplace needs a state")
     prob = problem(B, 1, H, HV, K, V, per_channel=per_channel, scale=scale,
-                   dtype="fp32" if q.dtype == torch.float32 else "bf16")
+                   dtype="fp32" if q.dtype == torch.float32 else "bf16", slab=slab)
     if out is not None:
         o, s = out
     else:

@@ -278,20 +278,34 @@ gdr_status check_ws(const Prob& r, const void* ws, size_t ws_bytes) {
   return GDR_OK;
 }
 
+// State columns per decode workgroup: 0 chooses (see decode_columns).
+int decode_columns(const gdr_problem* p) {
+  if (p->scan_slab != 0) return p->scan_slab < p->V ? p->scan_slab : p->V;
+  return p->V;   // whole rows: measured best or equal on the decode batches
+}
+
+template <int K, int V, int VB, bool PERCH>
+gdr_status launch_decode_kvb(bool f32, DecodeArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)a.B * a.HV * (V / VB));
+  if (f32) return launch(decode_step_kernel<K, V, VB, PERCH, float>, grid, 256, a, s);
+  return launch(decode_step_kernel<K, V, VB, PERCH, uint16_t>, grid, 256, a, s);
+}
+
 template <int K, int V, bool PERCH>
-gdr_status launch_decode_kv(bool f32, DecodeArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((size_t)a.B * a.HV);
-  if (f32) return launch(decode_step_kernel<K, V, PERCH, float>, grid, 256, a, s);
-  return launch(decode_step_kernel<K, V, PERCH, uint16_t>, grid, 256, a, s);
+gdr_status launch_decode_kv(int vb, bool f32, DecodeArgs& a, hipStream_t s) {
+  if (vb == 32) return launch_decode_kvb<K, V, 32, PERCH>(f32, a, s);
+  if constexpr (V == 128)
+    if (vb == 128) return launch_decode_kvb<K, V, 128, PERCH>(f32, a, s);
+  return launch_decode_kvb<K, V, 64, PERCH>(f32, a, s);
 }
 
 template <bool PERCH>
-gdr_status launch_decode_p(int K, int V, bool f32, DecodeArgs& a, hipStream_t s) {
+gdr_status launch_decode_p(int K, int V, int vb, bool f32, DecodeArgs& a, hipStream_t s) {
   if (K == 64)
-    return V == 64 ? launch_decode_kv<64, 64, PERCH>(f32, a, s)
-                   : launch_decode_kv<64, 128, PERCH>(f32, a, s);
-  return V == 64 ? launch_decode_kv<128, 64, PERCH>(f32, a, s)
-                 : launch_decode_kv<128, 128, PERCH>(f32, a, s);
+    return V == 64 ? launch_decode_kv<64, 64, PERCH>(vb, f32, a, s)
+                   : launch_decode_kv<64, 128, PERCH>(vb, f32, a, s);
+  return V == 64 ? launch_decode_kv<128, 64, PERCH>(vb, f32, a, s)
+                 : launch_decode_kv<128, 128, PERCH>(vb, f32, a, s);
 }
 
 }  // namespace
@@ -309,7 +323,9 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   if ((p->g_per_channel != 0 && p->g_per_channel != 1) || !std::isfinite(p->scale))
     return GDR_ERR_ARG;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
-  if ((uint64_t)p->B * p->HV > 0x7fffffffull) return GDR_ERR_SHAPE;
+  if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64 && p->scan_slab != 128)
+    return GDR_ERR_ARG;
+  if ((uint64_t)p->B * p->HV * 4 > 0x7fffffffull) return GDR_ERR_SHAPE;
   if (!q || !k || !v || !g || !beta || !state_out || !o) return GDR_ERR_NULL;
   for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
                           (const void*)beta, (const void*)state_in, (const void*)state_out,
@@ -336,8 +352,9 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   a.scale = p->scale;
   const bool f32 = p->qkv_dtype == GDR_F32;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  return p->g_per_channel ? launch_decode_p<true>(p->K, p->V, f32, a, hs)
-                          : launch_decode_p<false>(p->K, p->V, f32, a, hs);
+  const int vb = decode_columns(p);
+  return p->g_per_channel ? launch_decode_p<true>(p->K, p->V, vb, f32, a, hs)
+                          : launch_decode_p<false>(p->K, p->V, vb, f32, a, hs);
 }
 
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {

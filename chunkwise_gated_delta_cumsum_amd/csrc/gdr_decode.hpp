@@ -9,13 +9,16 @@
 //   o  = scale S'^T q = scale ((diag(d) S)^T q + beta u (q . k))
 //
 // The step reads and writes the K x V fp32 state once; every other operand is
-// a vector, so the kernel is bound by HBM bandwidth on the state.  One
-// workgroup of four waves per (batch, value head): a lane owns four
-// consecutive state columns of K/4/RPI rows (RPI rows per wave instruction,
-// V/4 lanes per row), loads them all up front as 16-byte pieces of whole
-// rows (coalesced), forms its partial column sums of k^T (dS) and q^T (dS),
-// and keeps the values in registers for the update, which it writes back
-// in place of the loads (so the state may be updated in place).
+// a vector, so the kernel is bound by HBM bandwidth on the state.  The
+// columns of one state are independent (each column's sums run over the K
+// rows only), so one workgroup of four waves takes VB columns of one
+// (batch, value head): a lane owns four consecutive columns of K/4/RPI rows
+// (RPI rows per wave instruction, VB/4 lanes per row), loads them all up
+// front as 16-byte pieces of rows (coalesced), forms its partial column sums
+// of k^T (dS) and q^T (dS), and keeps the values in registers for the
+// update, which it writes back in place of the loads (so the state may be
+// updated in place).  Narrow slabs give more workgroups per state, which
+// keeps more of them in flight when the batch is small.
 #pragma once
 #include "gdr_device.hpp"
 
@@ -45,19 +48,20 @@ __device__ __forceinline__ float decode_in<uint16_t>(const void* p, size_t i) {
   return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);   // bf16 bits
 }
 
-template <int K, int V, bool PERCH, class IN>
+template <int K, int V, int VB, bool PERCH, class IN>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
-  constexpr int LPR = V / 4;        // lanes per state row
+  constexpr int LPR = VB / 4;       // lanes per state row
   constexpr int RPI = 64 / LPR;     // rows per wave instruction
   constexpr int RW = K / 4;         // rows per wave
   constexpr int IT = RW / RPI;      // float4 pieces per lane
   static_assert(RW % RPI == 0, "decode tile shape");
-  __shared__ __attribute__((aligned(16))) float sq[K], sk[K], sd[K], sv[V];
+  __shared__ __attribute__((aligned(16))) float sq[K], sk[K], sd[K], sv[VB];
   __shared__ f32x4 sA[4][LPR], sB[4][LPR];
   __shared__ float sqk;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / (V / VB);
+  const int v0 = (blockIdx.x % (V / VB)) * VB;   // first column of this slab
   const int b = bh / a.HV, hv = bh % a.HV;
   const int h = hv / (a.HV / a.H);
   const int c4 = lane % LPR;                 // columns 4 c4 .. 4 c4 + 3
@@ -69,7 +73,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   if (a.s_in) {
 #pragma unroll
     for (int it = 0; it < IT; ++it)
-      s[it] = *reinterpret_cast<const f32x4*>(a.s_in + sbase + (size_t)(r0 + RPI * it) * V + 4 * c4);
+      s[it] = *reinterpret_cast<const f32x4*>(a.s_in + sbase + (size_t)(r0 + RPI * it) * V + v0 +
+                                              4 * c4);
   } else {
 #pragma unroll
     for (int it = 0; it < IT; ++it) s[it] = zero4();
@@ -82,7 +87,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     sk[tid] = decode_in<IN>(a.k, qk0 + tid);
     sd[tid] = __expf(PERCH ? a.g[(size_t)bh * K + tid] : a.g[bh]);
   }
-  if (tid >= 128 && tid - 128 < V) sv[tid - 128] = decode_in<IN>(a.v, (size_t)bh * V + tid - 128);
+  if (tid >= 128 && tid - 128 < VB)
+    sv[tid - 128] = decode_in<IN>(a.v, (size_t)bh * V + v0 + tid - 128);
   __syncthreads();
   if (wave == 0) {
     float x = 0.f;
@@ -120,13 +126,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * c4);
   const f32x4 u = vv - A;
   if (wave == 0 && lane < LPR)
-    *reinterpret_cast<f32x4*>(a.o + (size_t)bh * V + 4 * c4) = a.scale * (Bq + (bt * sqk) * u);
+    *reinterpret_cast<f32x4*>(a.o + (size_t)bh * V + v0 + 4 * c4) =
+        a.scale * (Bq + (bt * sqk) * u);
   const f32x4 bu = bt * u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int row = r0 + RPI * it;
     __builtin_nontemporal_store(s[it] + sk[row] * bu, reinterpret_cast<f32x4*>(
-                                    a.s_out + sbase + (size_t)row * V + 4 * c4));
+                                    a.s_out + sbase + (size_t)row * V + v0 + 4 * c4));
   }
 }
 

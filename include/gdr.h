@@ -69,7 +69,8 @@ typedef enum gdr_status {
   GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
   GDR_ERR_HIP = 8,         /* a HIP query or kernel launch failed */
   GDR_ERR_ARG = 9,         /* scale not finite, g_per_channel not 0/1,
-                              scan_segments < 0 or scan_slab not 0, 32 or 64 */
+                              scan_segments < 0, or scan_slab not 0, 32 or 64
+                              (gdr_decode_step also takes 128) */
   GDR_ERR_ALIAS = 10       /* an output overlaps an input or the other output
                               (final_state == initial_state exactly is allowed) */
 } gdr_status;
@@ -153,8 +154,11 @@ gdr_status gdr_chunk_scan(const gdr_problem* p,
  *     o  = scale S'^T q
  * (sec-03 notes: the naive recurrence the chunkwise form equals; "Chunkwise
  * parallel algorithms" page, section 2.1: the delta rule).  The problem
- * takes T = 1 (GDR_ERR_SHAPE otherwise); chunk, scan_segments and scan_slab
- * are ignored.  Layouts are those of gdr_chunk_fwd with the token axis of
+ * takes T = 1 (GDR_ERR_SHAPE otherwise); chunk and scan_segments are
+ * ignored, and scan_slab sets the state columns per workgroup (0 chooses,
+ * or 32, 64 or 128; capped at V; any other value is GDR_ERR_ARG): each
+ * column's update depends on its own K entries only, so the width only
+ * spreads one state over more or fewer workgroups.  Layouts are those of gdr_chunk_fwd with the token axis of
  * extent 1:
  *   q, k  [B, H, K]  qkv_dtype        v  [B, HV, V]  qkv_dtype
  *   g     [B, HV] or [B, HV, K] fp32  beta [B, HV]   fp32

@@ -216,6 +216,7 @@ def test_decode_validation(lib):
     assert name(call_decode(lib, ok, o=7 * A)) == "GDR_ERR_ALIAS"
     assert name(call_decode(lib, ok, s_out=A)) == "GDR_ERR_ALIAS"
     assert name(call_decode(lib, ok, s_out=6 * A + 1024)) == "GDR_ERR_ALIAS"
+    assert name(call_decode(lib, base(T=1, slab=48))) == "GDR_ERR_ARG"
     # the chunk settings do not apply to a single token
     odd = base(T=1, B=2, H=2, HV=4, chunk=32, segments=5)
     assert name(call_decode(lib, odd, q=A + 4)) == "GDR_ERR_ALIGN"

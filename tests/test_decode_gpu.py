@@ -92,6 +92,21 @@ def test_prefill_then_decode(gpu_lib, w):
     check(o[:, T1:], s.cpu().numpy(), ro[:, T1:], rs, w.dtype, f"{w.name} prefill {T1} + 6")
 
 
+@pytest.mark.parametrize("slab", [32, 64, 128])
+@pytest.mark.parametrize("w", [WORKLOADS[3].with_(B=2, T=1, s0_std=0.1),
+                               WORKLOADS[2].with_(B=2, T=1, K=64, V=64, s0_std=0.1)],
+                         ids=["gqa", "kda_K64V64"])
+def test_decode_column_slabs(gpu_lib, w, slab):
+    """Every workgroup width gives the oracle's result (the widths sum a
+    column's rows in different orders, so the bits may differ)."""
+    import torch
+    inp = make_inputs(w)
+    o, s = gpu_lib.gdr_decode_step(*token(inp, 0), dev(inp.s0), scale=inp.scale, slab=slab)
+    torch.cuda.synchronize()
+    ro, rs = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.s0)
+    check(o.cpu().numpy(), s.cpu().numpy(), ro[:, 0], rs, w.dtype, f"{w.name} slab={slab}")
+
+
 def test_decode_inplace_and_zero_state(gpu_lib):
     import torch
     w = WORKLOADS[3].with_(B=2, T=1, s0_std=0.1)
