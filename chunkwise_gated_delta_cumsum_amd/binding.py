@@ -32,7 +32,8 @@ class GdrProblem(ctypes.Structure):
                 ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("g_per_channel", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32),
-                ("scan_segments", ctypes.c_int32), ("scan_slab", ctypes.c_int32)]
+                ("scan_segments", ctypes.c_int32), ("scan_slab", ctypes.c_int32),
+                ("qk_l2norm", ctypes.c_int32)]
 
 
 class GdrError(RuntimeError):
@@ -89,10 +90,12 @@ def check(status: int) -> None:
 
 def problem(B: int, T: int, H: int, HV: int, K: int, V: int, *, chunk: int = 64,
             per_channel: bool = False, scale: Optional[float] = None,
-            dtype: str = "bf16", segments: int = 0, slab: int = 0) -> GdrProblem:
+            dtype: str = "bf16", segments: int = 0, slab: int = 0,
+            qk_l2norm: bool = False) -> GdrProblem:
     return GdrProblem(B, T, H, HV, K, V, chunk, int(bool(per_channel)),
                       float(K ** -0.5 if scale is None else scale),
-                      {"fp32": GDR_F32, "bf16": GDR_BF16}[dtype], int(segments), int(slab))
+                      {"fp32": GDR_F32, "bf16": GDR_BF16}[dtype], int(segments), int(slab),
+                      int(bool(qk_l2norm)))
 
 
 def scan_segments(prob: GdrProblem) -> int:
@@ -113,7 +116,8 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0) -> GdrProblem:
+def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
+                  qk_l2norm=False) -> GdrProblem:
     import torch
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
@@ -142,7 +146,7 @@ def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0) -> GdrProb
             raise TypeError(f"{name} must be float32")
     return problem(B, T, H, HV, K, V, chunk=chunk, per_channel=per_channel, scale=scale,
                    dtype="fp32" if q.dtype == torch.float32 else "bf16", segments=segments,
-                   slab=slab)
+                   slab=slab, qk_l2norm=qk_l2norm)
 
 
 def _check_tensors(dev, **ts):
@@ -162,7 +166,8 @@ def _stream(dev) -> ctypes.c_void_p:
 
 def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
                   scale: Optional[float] = None, *, output_final_state: bool = True,
-                  workspace=None, out=None, segments: int = 0, slab: int = 0
+                  workspace=None, out=None, segments: int = 0, slab: int = 0,
+                  qk_l2norm: bool = False
                   ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunkwise gated delta rule forward on the GPU.
 
@@ -173,13 +178,14 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     ``workspace`` (uint8, at least workspace_size bytes) and ``out`` = (o, S)
     may be passed to avoid allocations.  ``segments`` > 0 asks for that many
     sequence segments in the state scan (0: automatic); ``slab`` (32 or 64)
-    sets the state columns per scan workgroup (0: automatic).
+    sets the state columns per scan workgroup (0: automatic).  ``qk_l2norm``
+    L2-normalises every q and k row inside the kernels first.
     """
     import torch
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if initial_state is not None and (initial_state.dtype != torch.float32 or
@@ -205,7 +211,8 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
 
 def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None, *,
                    V: Optional[int] = None, inspect: bool = False,
-                   workspace=None, segments: int = 0, slab: int = 0
+                   workspace=None, segments: int = 0, slab: int = 0,
+                   qk_l2norm: bool = False
                    ) -> Tuple["torch.Tensor", Dict[str, "torch.Tensor"]]:
     """Run the chunk-preparation stage alone.
 
@@ -216,7 +223,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, g=g, beta=beta)
-    prob = _problem_from(q, k, None, g, beta, chunk, scale, segments, slab)
+    prob = _problem_from(q, k, None, g, beta, chunk, scale, segments, slab, qk_l2norm)
     if V is not None:
         prob.V = V
     nbytes = workspace_size(prob)
@@ -242,7 +249,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
 
 def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 64,
                    scale: Optional[float] = None, *, out=None, segments: int = 0,
-                   slab: int = 0):
+                   slab: int = 0, qk_l2norm: bool = False):
     """Run the state-scan stage on a workspace filled by gdr_chunk_prep.
 
     ``out`` = (o, final_state) reuses caller tensors (final_state may be None).
@@ -251,7 +258,7 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if out is not None:
@@ -266,7 +273,7 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
 
 
 def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None, *,
-                    out=None, inplace: bool = False, slab: int = 0
+                    out=None, inplace: bool = False, slab: int = 0, qk_l2norm: bool = False
                     ) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """One decode step (one token per sequence) on the GPU.
 
@@ -276,7 +283,8 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     K**-0.5.  Returns (o [B, HV, V] float32, new state [B, HV, K, V] float32).
     With ``inplace`` the new state overwrites ``state``; ``out`` = (o, S) may
     be passed to avoid allocations.  ``slab`` (32, 64 or 128) sets the state
-    columns per workgroup (0: automatic).
+    columns per workgroup (0: automatic).  ``qk_l2norm`` L2-normalises q and
+    k inside the kernel first.
     """
     import torch
     lib = load()
@@ -308,7 +316,8 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     if inplace and state is None:
         raise ValueError("inplace needs a state")
     prob = problem(B, 1, H, HV, K, V, per_channel=per_channel, scale=scale,
-                   dtype="fp32" if q.dtype == torch.float32 else "bf16", slab=slab)
+                   dtype="fp32" if q.dtype == torch.float32 else "bf16", slab=slab,
+                   qk_l2norm=qk_l2norm)
     if out is not None:
         o, s = out
     else:

@@ -27,6 +27,7 @@ struct Prob {
   size_t es;        // bytes per q/k/v element and per workspace fragment element
   int nseg, seg_len; // sequence segments of the state scan
   int bv;            // state columns per scan workgroup (32 or 64)
+  bool l2norm;       // L2-normalise the q and k rows in the prep kernels
 };
 
 // Number of sequence segments for the state scan.  One segment runs the
@@ -73,6 +74,7 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
     return GDR_ERR_SHAPE;
   if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
   if (p->g_per_channel != 0 && p->g_per_channel != 1) return GDR_ERR_ARG;
+  if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDR_ERR_ARG;
   if (!std::isfinite(p->scale)) return GDR_ERR_ARG;
   if (p->chunk != kChunk) return GDR_ERR_UNSUPPORTED;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
@@ -82,6 +84,7 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.perch = p->g_per_channel == 1;
   r.f32 = p->qkv_dtype == GDR_F32;
   r.scale = p->scale;
+  r.l2norm = p->qk_l2norm == 1;
   r.es = r.f32 ? 4 : 2;
   if (p->scan_segments < 0) return GDR_ERR_ARG;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
@@ -252,6 +255,7 @@ PrepArgs prep_args(const Prob& r, const void* q, const void* k, const float* g,
   a.scale = r.scale;
   a.wt = base + L.wt; a.ah = base + L.ah; a.rs = reinterpret_cast<float*>(base + L.rs);
   a.qh = base + L.qh; a.kh = base + L.kh;
+  a.l2norm = r.l2norm ? 1 : 0;
   a.d_gamma = a.d_akk = a.d_aqk = a.d_minv = nullptr;
   return a;
 }
@@ -320,7 +324,8 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
       p->HV % p->H != 0)
     return GDR_ERR_SHAPE;
   if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
-  if ((p->g_per_channel != 0 && p->g_per_channel != 1) || !std::isfinite(p->scale))
+  if ((p->g_per_channel != 0 && p->g_per_channel != 1) ||
+      (p->qk_l2norm != 0 && p->qk_l2norm != 1) || !std::isfinite(p->scale))
     return GDR_ERR_ARG;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64 && p->scan_slab != 128)
@@ -350,6 +355,7 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   a.s_in = state_in; a.s_out = state_out; a.o = o;
   a.B = p->B; a.H = p->H; a.HV = p->HV;
   a.scale = p->scale;
+  a.l2norm = p->qk_l2norm;
   const bool f32 = p->qkv_dtype == GDR_F32;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int vb = decode_columns(p);
@@ -459,7 +465,7 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace NULL or smaller than gdr_chunk_fwd_workspace_size";
     case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE: the current HIP device is not gfx950";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP query or kernel launch failed";
-    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel 0 or 1, scan_segments >= 0, scan_slab 0, 32 or 64";
+    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel and qk_l2norm 0 or 1, scan_segments >= 0, scan_slab 0, 32 or 64 (128 for decode)";
     case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: an output overlaps an input or another output";
     default: return "GDR_ERR_UNKNOWN: unknown status value";
   }

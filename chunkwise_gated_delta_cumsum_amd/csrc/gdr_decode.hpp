@@ -8,6 +8,9 @@
 //   u  = v - (diag(d) S)^T k
 //   o  = scale S'^T q = scale ((diag(d) S)^T q + beta u (q . k))
 //
+// optionally with q and k L2-normalised first (x rsqrt(sum x^2 + 1e-6)),
+// which the kernel applies as factors on the raw rows' sums, in fp32.
+//
 // The step reads and writes the K x V fp32 state once; every other operand is
 // a vector, so the kernel is bound by HBM bandwidth on the state.  The
 // columns of one state are independent (each column's sums run over the K
@@ -35,6 +38,7 @@ struct DecodeArgs {
   float* o;              // [B, HV, V]
   int B, H, HV;
   float scale;
+  int l2norm;            // 1: L2-normalise q and k first
 };
 
 template <class T>
@@ -57,7 +61,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   static_assert(RW % RPI == 0, "decode tile shape");
   __shared__ __attribute__((aligned(16))) float sq[K], sk[K], sd[K], sv[VB];
   __shared__ f32x4 sA[4][LPR], sB[4][LPR];
-  __shared__ float sqk;
+  __shared__ float sqk, srq, srk;   // q . k and the row normalisers of q and k
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int bh = blockIdx.x / (V / VB);
@@ -91,11 +95,27 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     sv[tid - 128] = decode_in<IN>(a.v, (size_t)bh * V + v0 + tid - 128);
   __syncthreads();
   if (wave == 0) {
-    float x = 0.f;
-    for (int i = lane; i < K; i += 64) x += sq[i] * sk[i];
+    float x = 0.f, nq = 0.f, nk = 0.f;
+    for (int i = lane; i < K; i += 64) {
+      x += sq[i] * sk[i];
+      nq += sq[i] * sq[i];
+      nk += sk[i] * sk[i];
+    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    if (lane == 0) sqk = x;
+    for (int off = 32; off > 0; off >>= 1) {
+      x += __shfl_xor(x, off, 64);
+      nq += __shfl_xor(nq, off, 64);
+      nk += __shfl_xor(nk, off, 64);
+    }
+    if (lane == 0) {
+      // with in-kernel normalisation, q^ = rq q and k^ = rk k: the sums
+      // below use the raw rows and take the factors afterwards
+      const float rq = a.l2norm ? rsqrtf(nq + kL2NormEps) : 1.f;
+      const float rk = a.l2norm ? rsqrtf(nk + kL2NormEps) : 1.f;
+      srq = rq;
+      srk = rk;
+      sqk = x * rq * rk;
+    }
   }
 
   // decay, then the partial column sums k^T (dS) and q^T (dS) of this lane
@@ -120,15 +140,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     sB[wave][c4] = Bq;
   }
   __syncthreads();
-  A = sA[0][c4] + sA[1][c4] + sA[2][c4] + sA[3][c4];
-  Bq = sB[0][c4] + sB[1][c4] + sB[2][c4] + sB[3][c4];
+  A = srk * (sA[0][c4] + sA[1][c4] + sA[2][c4] + sA[3][c4]);
+  Bq = srq * (sB[0][c4] + sB[1][c4] + sB[2][c4] + sB[3][c4]);
   const float bt = a.beta[bh];
   const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * c4);
   const f32x4 u = vv - A;
   if (wave == 0 && lane < LPR)
     *reinterpret_cast<f32x4*>(a.o + (size_t)bh * V + v0 + 4 * c4) =
         a.scale * (Bq + (bt * sqk) * u);
-  const f32x4 bu = bt * u;
+  const f32x4 bu = (bt * srk) * u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int row = r0 + RPI * it;

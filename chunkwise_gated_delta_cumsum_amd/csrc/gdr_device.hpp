@@ -72,6 +72,30 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
+// Optional L2 normalisation of query and key rows inside the kernels, with
+// the normaliser of the scalar-g kernel page: x * rsqrt(sum(x^2) + 1e-6).
+// The sums run in fp32, and the factor multiplies the raw row in fp32
+// wherever its values enter a product or an fp16 operand.
+constexpr float kL2NormEps = 1e-6f;
+
+// Sum of squares of the input elements in 16 bytes (8 bf16 or 4 fp32).
+template <class IN>
+__device__ __forceinline__ float sumsq16(u32x4 v) {
+  float s = 0.f;
+  if constexpr (sizeof(IN) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+      s += lo * lo + hi * hi;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += __uint_as_float(v[i]) * __uint_as_float(v[i]);
+  }
+  return s;
+}
+
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Index of this wave in its workgroup, as a scalar.  Branches on it are then
@@ -144,6 +168,13 @@ struct PolicyF16 {
   }
   __device__ static __forceinline__ float in_to_f32(in_t x) { return bf16_to_f32(x); }
   __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return bf16_to_f32(x[i]); }
+  // raw elements times f (fp32), rounded once to the fragment type
+  __device__ static __forceinline__ frag_t frag_scaled(raw_t x, float f) {
+    frag_t r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)(bf16_to_f32(x[i]) * f);
+    return r;
+  }
   // 16x16 tile += (16 x 16) * (16 x 16), lane holds k = 4*grp + i; fp16
   // operands (the inverse is consumed as fp16 anyway), fp32 accumulation
   __device__ static __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {
@@ -189,6 +220,7 @@ struct PolicyF32 {
     return f;
   }
   __device__ static __forceinline__ frag_t frag_from_raw(raw_t x) { return x; }
+  __device__ static __forceinline__ frag_t frag_scaled(raw_t x, float f) { return x * f; }
   __device__ static __forceinline__ float in_to_f32(in_t x) { return x; }
   __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return x[i]; }
   __device__ static __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {

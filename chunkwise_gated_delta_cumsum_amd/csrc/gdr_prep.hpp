@@ -39,6 +39,7 @@ struct PrepArgs {
   float* rs;
   void* qh;
   void* kh;
+  int l2norm;      // 1: L2-normalise every q and k row first
   float* d_gamma;  // optional inspection outputs (fp32)
   float* d_akk;
   float* d_aqk;
@@ -258,7 +259,8 @@ __device__ __forceinline__ void dump_minv(float* out, const float* sMT, int tid)
 template <int W, int K, class P>
 __device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typename P::in_t* sQ,
                                            float* sL, const float* sGam, const float* sBeta,
-                                           float scale, int r, int grp, f32x4 (&aqT)[4]) {
+                                           const float* sRq, const float* sRk, float scale,
+                                           int r, int grp, f32x4 (&aqT)[4]) {
   using in_t = typename P::in_t;
   using gfrag_t = std::conditional_t<P::kF32, f32x8, bf16x8>;
   constexpr int KB = K / 32;
@@ -273,15 +275,19 @@ __device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typ
 
   // gamma and beta of the rows this lane touches: rows 16X + 4grp + (0..3)
   // of the accumulator and row 16X + r of the columns, for every block X
-  f32x4 g4[4], b4[4];
+  // (beta and the row factors of k on the k rows; the q row factor on
+  // column i of A_qk^T; all 1 without in-kernel normalisation)
+  f32x4 g4[4], b4[4], rk4[4];
   float g1[4], b1[4];
 #pragma unroll
   for (int X = 0; X < 4; ++X) {
     g4[X] = *reinterpret_cast<const f32x4*>(sGam + 16 * X + 4 * grp);
-    b4[X] = *reinterpret_cast<const f32x4*>(sBeta + 16 * X + 4 * grp);
+    rk4[X] = *reinterpret_cast<const f32x4*>(sRk + 16 * X + 4 * grp);
+    b4[X] = *reinterpret_cast<const f32x4*>(sBeta + 16 * X + 4 * grp) * rk4[X];
     g1[X] = sGam[16 * X + r];
-    b1[X] = sBeta[16 * X + r];
+    b1[X] = sBeta[16 * X + r] * sRk[16 * X + r];
   }
+  const float rq1 = sRq[16 * W + r];
 
   auto frag = [&](const in_t* row) -> gfrag_t {
     if constexpr (P::kF32)
@@ -313,7 +319,7 @@ __device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typ
       // A_qk^T tile (X, W): rows c' = 16X + 4grp + j4 (k), column i = 16W + r (q)
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        const float x = acc[j4] * b4[X][j4] * scale * __expf(g1[W] - g4[X][j4]);
+        const float x = acc[j4] * b4[X][j4] * (scale * rq1) * __expf(g1[W] - g4[X][j4]);
         val[j4] = (X < W || 4 * grp + j4 <= r) ? x : 0.f;
       }
       aqT[X] = val;
@@ -321,7 +327,7 @@ __device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typ
       // A_kk tile (X, Y): rows i = 16X + 4grp + j4, column j = 16Y + r
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        const float x = acc[j4] * b1[Y] * __expf(g4[X][j4] - g1[Y]);
+        const float x = acc[j4] * b1[Y] * rk4[X][j4] * __expf(g4[X][j4] - g1[Y]);
         sL[(16 * X + 4 * grp + j4) * LP + 16 * Y + r] = (X > Y || 4 * grp + j4 > r) ? x : 0.f;
       }
     }
@@ -358,6 +364,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   __shared__ float sGam[C];
   __shared__ float sBeta[C];
   __shared__ float sKs[C];     // beta_c exp(gamma_last - gamma_c)
+  __shared__ float sRq[C];     // row factors of q and k (L2 normalisation; else 1)
+  __shared__ float sRk[C];
   float* sMT = reinterpret_cast<float*>(sQbuf);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -391,6 +399,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       const size_t idx = ((size_t)b * T + t) * a.HV + hv;
       gv = a.g[idx];
       bv = a.beta[idx];
+    }
+  }
+
+  // ---- optional L2 normalisation of the q and k rows -----------------------
+  // The rows stay raw in LDS; each row's factor rsqrt(sum x^2 + 1e-6) (1 when
+  // normalisation is off) multiplies it in fp32 wherever its values enter a
+  // product or an fp16 operand: the Gram entries, the W^ row scalars and the
+  // q/k fragments of the scan.  In each load round the VPR consecutive
+  // threads c VPR .. c VPR + VPR-1 hold row c (VPR divides the wave), so a
+  // row's sum of squares is a butterfly over VPR lanes.
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    float fq = 1.f, fk = 1.f;
+    if (a.l2norm) {
+      float sq = sumsq16<in_t>(__builtin_bit_cast(u32x4, qv[i]));
+      float sk = sumsq16<in_t>(__builtin_bit_cast(u32x4, kv[i]));
+#pragma unroll
+      for (int off = 1; off < VPR; off <<= 1) {
+        sq += __shfl_xor(sq, off, 64);
+        sk += __shfl_xor(sk, off, 64);
+      }
+      fq = rsqrtf(sq + kL2NormEps);
+      fk = rsqrtf(sk + kL2NormEps);
+    }
+    const int e = tid + 256 * i;
+    if (e % VPR == 0) {
+      sRq[e / VPR] = fq;
+      sRk[e / VPR] = fk;
     }
   }
 
@@ -436,10 +472,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     for (int pc = tid; pc < C * K / 8; pc += 256) {
       const int ln = pc & 63, tkb = pc >> 6;
       const int row = 16 * (tkb / KB) + (ln & 15), ch = 32 * (tkb % KB) + 8 * (ln >> 4);
-      __builtin_nontemporal_store(P::frag_from_raw(P::load_raw8(sQ + row * KP + ch)),
-                                  reinterpret_cast<frag_t*>(qd + (size_t)pc * 8));
-      __builtin_nontemporal_store(P::frag_from_raw(P::load_raw8(sK + row * KP + ch)),
-                                  reinterpret_cast<frag_t*>(kd + (size_t)pc * 8));
+      const auto qraw = P::load_raw8(sQ + row * KP + ch), kraw = P::load_raw8(sK + row * KP + ch);
+      // normalised rows: the raw values times the row factor, in fp32, then
+      // rounded once to the fragment type
+      const frag_t qf = a.l2norm ? P::frag_scaled(qraw, sRq[row]) : P::frag_from_raw(qraw);
+      const frag_t kf = a.l2norm ? P::frag_scaled(kraw, sRk[row]) : P::frag_from_raw(kraw);
+      __builtin_nontemporal_store(qf, reinterpret_cast<frag_t*>(qd + (size_t)pc * 8));
+      __builtin_nontemporal_store(kf, reinterpret_cast<frag_t*>(kd + (size_t)pc * 8));
     }
   }
 
@@ -448,10 +487,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) aqT[j] = zero4();
   switch (wave) {
-    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
-    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
-    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
-    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, a.scale, r, grp, aqT); break;
+    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
+    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
+    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
+    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
   }
 
   lds_barrier();   // sL complete
@@ -475,7 +514,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   // ---- 4a. W^ (beta exp(gamma_last - gamma) scales the rows of M^-T) -------
   fold_w<K, P, true>(sMT, static_cast<ws_t*>(a.wt) + (size_t)cid * K * C, wave, lane, r, grp,
                      [&](int c, int d) { return P::in_to_f32(sK[c * KP + d]); },
-                     [&](int c) { return sKs[c]; });
+                     [&](int c) { return sKs[c] * sRk[c]; });
   GDR_PPROF(5);
 
   // ---- 4b. A^ ----------------------------------------------------------------

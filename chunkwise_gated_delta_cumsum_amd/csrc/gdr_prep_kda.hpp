@@ -159,6 +159,28 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       kr[kb] = P::load_raw8(reinterpret_cast<const in_t*>(stg + (16 + r) * QSR) + 32 * kb + 8 * grp);
     }
   }
+  // optional L2 normalisation of this lane's q and k row: its channels are
+  // spread over the lanes r, r + 16, r + 32, r + 48 (grp), 8 per k block.
+  // The raw values stay in registers; the row factors rsqrt(sum x^2 + 1e-6)
+  // multiply them in fp32 where they are converted below (1 when off).
+  float fq = 1.f, fk = 1.f;
+  if (a.l2norm) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = P::raw_f32(qr[kb], j), y = P::raw_f32(kr[kb], j);
+        sq += x * x;
+        sk += y * y;
+      }
+    sq += __shfl_xor(sq, 16, 64);
+    sk += __shfl_xor(sk, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    sk += __shfl_xor(sk, 32, 64);
+    fq = rsqrtf(sq + kL2NormEps);
+    fk = rsqrtf(sk + kL2NormEps);
+  }
   if (!valid) bv = 0.f;
 
   // ---- 1. in-block cumsum ----------------------------------------------------
@@ -223,8 +245,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       const float s15 = j < 4 ? t15a[j] : t15b[j - 4];
       const float sm = j < 4 ? tma[j] : tmb[j - 4];
       const float x = s[kb][j];
-      const float qv = valid ? P::raw_f32(qr[kb], j) : 0.f;
-      const float kv = valid ? P::raw_f32(kr[kb], j) : 0.f;
+      const float qv = valid ? P::raw_f32(qr[kb], j) * fq : 0.f;
+      const float kv = valid ? P::raw_f32(kr[kb], j) * fk : 0.f;
       const float el = __expf(x);
       kl[kb][j] = kv * el;
       ql[kb][j] = qv * el;
@@ -257,8 +279,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float qv = valid ? P::raw_f32(qr[kb], j) : 0.f;
-          const float kv = valid ? P::raw_f32(kr[kb], j) : 0.f;
+          const float qv = valid ? P::raw_f32(qr[kb], j) * fq : 0.f;
+          const float kv = valid ? P::raw_f32(kr[kb], j) * fk : 0.f;
           const float kj = __shfl(kv, src, 64);
           const float sj = __shfl(s[kb][j], src, 64);
           const float e = __expf(s[kb][j] - sj);

@@ -10,7 +10,10 @@ DeltaNet chunk kernel page, whose demo uses seed 42, normal q/k/v, sigmoid
 beta and a state scaled by 0.1):
 
 * q, k ~ N(0, 1) on [B, T, H, K], then each row is L2-normalised with
-  x * rsqrt(sum(x^2) + 1e-6) (the normaliser of the scalar-g kernel page);
+  x * rsqrt(sum(x^2) + 1e-6) (the normaliser of the scalar-g kernel page),
+  unless the workload asks for raw rows (normalize_qk=False, for the
+  in-kernel normalisation tests, where the rows are normalised on the
+  device and in the oracle instead);
 * v ~ N(0, 1) on [B, T, HV, V];
 * beta = sigmoid(N(0, 1)) on [B, T, HV];
 * g = logsigmoid(N(mu, 1)) on [B, T, HV] (one log-decay per value head) or on
@@ -48,6 +51,7 @@ class Workload:
     g_mu: float = 3.0            # g = logsigmoid(N(g_mu, 1))
     s0_std: float = 0.0          # 0 -> no initial state
     seed: int = 42
+    normalize_qk: bool = True    # False: raw N(0, 1) q and k (for in-kernel normalisation)
 
     @property
     def G(self) -> int:
@@ -165,8 +169,10 @@ def make_inputs(w: Workload, T: Optional[int] = None) -> Inputs:
         w = w.with_(T=T)
     rng = np.random.default_rng(w.seed)
     B, T_, H, HV, K, V = w.B, w.T, w.H, w.HV, w.K, w.V
-    q = _l2norm_rows(rng.standard_normal((B, T_, H, K)))
-    k = _l2norm_rows(rng.standard_normal((B, T_, H, K)))
+    q = rng.standard_normal((B, T_, H, K))
+    k = rng.standard_normal((B, T_, H, K))
+    if w.normalize_qk:
+        q, k = _l2norm_rows(q), _l2norm_rows(k)
     v = rng.standard_normal((B, T_, HV, V))
     beta = _sigmoid(rng.standard_normal((B, T_, HV))).astype(np.float32)
     gshape = (B, T_, HV, K) if w.per_channel else (B, T_, HV)

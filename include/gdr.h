@@ -68,7 +68,7 @@ typedef enum gdr_status {
   GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query */
   GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
   GDR_ERR_HIP = 8,         /* a HIP query or kernel launch failed */
-  GDR_ERR_ARG = 9,         /* scale not finite, g_per_channel not 0/1,
+  GDR_ERR_ARG = 9,         /* scale not finite, g_per_channel or qk_l2norm not 0/1,
                               scan_segments < 0, or scan_slab not 0, 32 or 64
                               (gdr_decode_step also takes 128) */
   GDR_ERR_ALIAS = 10       /* an output overlaps an input or the other output
@@ -91,6 +91,13 @@ typedef struct gdr_problem {
                                 automatically (gdr_chunk_scan_slab), or 32 or 64;
                                 any width gives the same result up to rounding
                                 order, it only moves work between workgroups */
+  int32_t qk_l2norm;         /* 1: L2-normalise every q and k row inside the
+                                kernels first, x * rsqrt(sum(x^2) + 1e-6) (the
+                                scalar-g kernel page's optional normaliser);
+                                the sums run in fp32 and each row's factor
+                                multiplies its raw values in fp32 wherever
+                                they enter a product.  0: q and k are used as
+                                given */
 } gdr_problem;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when

@@ -14,15 +14,19 @@ arithmetic.
                      order, exposing gamma, A_kk, M, W, U, A_qk.
 * ``ut_inverse_*``-- three forms of the UT inverse (triangular solve, Neumann
                      series, row iteration) that the pages state are equal.
+* ``l2norm_rows`` -- fp64 row normaliser x * rsqrt(sum x^2 + 1e-6), the
+                     reference for in-kernel q/k normalisation.
 
 Pins (tests/test_oracle_*.py, CPU only): chunk form == recurrence for several
 chunk sizes, closed forms (beta = 0 and g = 0; orthonormal keys; repeated
 unit key; reset by g = -800; standard-basis keys with per-channel decay),
 a Kronecker-product brute force on tiny shapes, segment splitting, joint
 linearity, grouped-head equivalence, hand-derived golden values, and the
-three UT inverse forms against each other.  No function here is left
-unpinned.
+three UT inverse forms against each other, and the row normaliser against a
+hand-derived row, its closed-form norm and the zero row.  No function here
+is left unpinned.
 """
 from .recurrence import build, num_threads, recurrence, recurrence_heads  # noqa: F401
 from .chunk_form import (chunk_forward, decayed_dot, ut_inverse_neumann,  # noqa: F401
                          ut_inverse_rowloop, ut_inverse_solve)
+from .l2norm import l2norm_rows  # noqa: F401

@@ -220,3 +220,15 @@ def test_decode_validation(lib):
     # the chunk settings do not apply to a single token
     odd = base(T=1, B=2, H=2, HV=4, chunk=32, segments=5)
     assert name(call_decode(lib, odd, q=A + 4)) == "GDR_ERR_ALIGN"
+
+
+def test_qk_l2norm_flag_validation(lib):
+    bad = base(T=100)
+    bad.qk_l2norm = 2
+    assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"
+    assert gdr.workspace_size(bad) == 0
+    bad1 = base(T=1)
+    bad1.qk_l2norm = -1
+    assert binding.STATUS_NAMES[call_decode(lib, bad1)] == "GDR_ERR_ARG"
+    ok = base(T=100, qk_l2norm=True)
+    assert ok.qk_l2norm == 1 and gdr.workspace_size(ok) == gdr.workspace_size(base(T=100))

@@ -1,0 +1,84 @@
+"""GPU parity with in-kernel q/k L2 normalisation (gdr_problem.qk_l2norm = 1,
+the scalar-g kernel page's optional normaliser): the device gets raw q and k
+rows; the oracle normalises the same raw values in fp64 (oracle.l2norm_rows)
+and runs the recurrence.  Bounds as for the other parity tests: 1e-3 for
+fp32 inputs, 2e-2 for bf16 inputs, on o and the final state.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from chunkwise_gated_delta_cumsum_amd.inputs import WORKLOADS, make_inputs
+from helpers import TOL, rel_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def check(o, s, ro, rs, dtype, label):
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    print(f"{label}: err_o={eo:.3e} err_S={es:.3e} (tol {TOL[dtype]})", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+def oracle_normalised(inp):
+    return oracle.recurrence(oracle.l2norm_rows(inp.q), oracle.l2norm_rows(inp.k), inp.v, inp.g,
+                             inp.beta, inp.scale, inp.s0)
+
+
+CASES = [
+    (WORKLOADS[1].with_(T=300, normalize_qk=False), 0),
+    (WORKLOADS[1].with_(T=1000, normalize_qk=False), 5),                  # ragged, segmented
+    (WORKLOADS[2].with_(B=1, T=200, normalize_qk=False), 0),              # per-channel decay
+    (WORKLOADS[2].with_(B=1, T=700, normalize_qk=False), 3),
+    (WORKLOADS[3].with_(B=1, T=640, normalize_qk=False), 3),              # grouped heads, S0
+    (WORKLOADS[0].with_(normalize_qk=False), 2),                          # fp32
+    (WORKLOADS[0].with_(normalize_qk=False, per_channel=True, g_mu=4.0), 1),
+]
+
+
+@pytest.mark.parametrize("w,segs", CASES, ids=[f"{w.name}-T{w.T}-seg{s_}" for w, s_ in CASES])
+def test_chunk_fwd_in_kernel_l2norm(gpu_lib, w, segs):
+    import torch
+    inp = make_inputs(w)
+    t = to_device(inp)
+    o, s = gpu_lib.gdr_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["initial_state"],
+                                 scale=inp.scale, segments=segs, qk_l2norm=True)
+    torch.cuda.synchronize()
+    ro, rs = oracle_normalised(inp)
+    check(o.cpu().numpy(), s.cpu().numpy(), ro, rs, w.dtype, f"{w.name} T={w.T}")
+
+
+def test_in_kernel_l2norm_large_rows(gpu_lib):
+    """Raw rows far from unit length (x 40) normalise to the same result."""
+    import torch
+    w = WORKLOADS[1].with_(T=200, normalize_qk=False)
+    inp = make_inputs(w)
+    t = to_device(inp)
+    q = (t["q"].float() * 40).to(t["q"].dtype)
+    k = (t["k"].float() * 40).to(t["k"].dtype)
+    o, s = gpu_lib.gdr_chunk_fwd(q, k, t["v"], t["g"], t["beta"], None, scale=inp.scale,
+                                 qk_l2norm=True)
+    torch.cuda.synchronize()
+    qr = q.float().cpu().numpy().astype(np.float64)
+    kr = k.float().cpu().numpy().astype(np.float64)
+    ro, rs = oracle.recurrence(oracle.l2norm_rows(qr), oracle.l2norm_rows(kr), inp.v, inp.g,
+                               inp.beta, inp.scale, None)
+    check(o.cpu().numpy(), s.cpu().numpy(), ro, rs, w.dtype, "raw rows x40")
+
+
+@pytest.mark.parametrize("w", [WORKLOADS[3].with_(B=3, T=1, s0_std=0.1, normalize_qk=False),
+                               WORKLOADS[2].with_(B=2, T=1, s0_std=0.1, normalize_qk=False),
+                               WORKLOADS[0].with_(B=2, T=1, s0_std=0.1, normalize_qk=False)],
+                         ids=["gqa", "kda", "fp32"])
+def test_decode_in_kernel_l2norm(gpu_lib, w):
+    import torch
+    inp = make_inputs(w)
+    t = to_device(inp)
+    o, s = gpu_lib.gdr_decode_step(t["q"][:, 0].contiguous(), t["k"][:, 0].contiguous(),
+                                   t["v"][:, 0].contiguous(), t["g"][:, 0].contiguous(),
+                                   t["beta"][:, 0].contiguous(), t["initial_state"],
+                                   scale=inp.scale, qk_l2norm=True)
+    torch.cuda.synchronize()
+    ro, rs = oracle_normalised(inp)
+    check(o.cpu().numpy(), s.cpu().numpy(), ro[:, 0], rs, w.dtype, f"decode {w.name}")

@@ -321,3 +321,28 @@ def test_chunk_intermediate_masks():
     assert np.any(np.diagonal(r["A_qk"], axis1=-2, axis2=-1) != 0)
     gam = r["gamma"][0, 0, :, :, 0]
     np.testing.assert_allclose(gam, np.cumsum(g[0, :, 0].reshape(2, 64), axis=1), atol=1e-14)
+
+
+def test_l2norm_rows_pins():
+    """The row normaliser of in-kernel q/k normalisation: a hand-derived row
+    ((3, 4) -> (3, 4) / sqrt(25 + 1e-6)), the closed-form norm of any output
+    row, ||x|| / sqrt(||x||^2 + 1e-6), the zero row staying zero, and
+    independence of the rows."""
+    import math
+    from oracle import l2norm_rows
+    got = l2norm_rows(np.array([[3.0, 4.0]]))
+    d = math.sqrt(25.0 + 1e-6)
+    assert got[0, 0] == 3.0 / d and got[0, 1] == 4.0 / d
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 5, 2, 16)) * rng.uniform(0.01, 10, (3, 5, 2, 1))
+    y = l2norm_rows(x)
+    nx = np.sqrt((x ** 2).sum(-1))
+    np.testing.assert_allclose(np.sqrt((y ** 2).sum(-1)), nx / np.sqrt(nx ** 2 + 1e-6),
+                               rtol=1e-13)
+    # direction kept: y is a positive multiple of x, row by row
+    np.testing.assert_allclose(y * (np.sqrt(nx ** 2 + 1e-6))[..., None], x, rtol=1e-12)
+    assert not l2norm_rows(np.zeros((2, 8))).any()
+    x2 = x.copy()
+    x2[0, 0, 0] *= 7.0
+    y2 = l2norm_rows(x2)
+    np.testing.assert_array_equal(y2[1:], y[1:])
