@@ -25,6 +25,13 @@
  * g_t is one scalar per (b, t, hv) or, for the per-channel (KDA) form, one
  * value per key channel; exp(g_t) then scales row d of S by exp(g_t[d]).
  *
+ * With linear = 1 the write has no prediction term (no erase):
+ *       S <- S + beta_t k_t v_t^T
+ * the decayed linear attention of the Mamba2 state-space-duality section of
+ * the "Chunkwise parallel algorithms" page (section 1.1: S_t = alpha_t
+ * S_{t-1} + v_t k_t^T, o_t = S_t q_t, with alpha_t = exp(g_t) and beta_t as
+ * an input scale; beta = 1 and scale = 1 give the page's form exactly).
+ *
  * Layouts (row-major, contiguous):
  *   q, k   [B, T, H, K]      v, o  [B, T, HV, V]
  *   g      [B, T, HV] or [B, T, HV, K]
@@ -49,12 +56,12 @@ int gdr_oracle_num_threads(void) {
 }
 
 /* Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
-int gdr_oracle_recurrence(int B, int T, int H, int HV, int K, int V,
-                          int g_per_channel, double scale,
-                          const double* q, const double* k, const double* v,
-                          const double* g, const double* beta,
-                          const double* s0, double* o, double* s_final,
-                          int num_threads) {
+int gdr_oracle_recurrence_rule(int B, int T, int H, int HV, int K, int V,
+                               int g_per_channel, int linear, double scale,
+                               const double* q, const double* k, const double* v,
+                               const double* g, const double* beta,
+                               const double* s0, double* o, double* s_final,
+                               int num_threads) {
   if (B < 1 || T < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
     return -1;
   if (!q || !k || !v || !g || !beta || !o || !s_final) return -1;
@@ -99,10 +106,11 @@ int gdr_oracle_recurrence(int B, int T, int H, int HV, int K, int V,
       for (int d = 0; d < K; ++d)
         for (int j = 0; j < V; ++j) S[(size_t)d * V + j] *= dec[d];
 
-      /* prediction p = S^T k_t */
+      /* prediction p = S^T k_t (none for the linear rule) */
       for (int j = 0; j < V; ++j) p[j] = 0.0;
-      for (int d = 0; d < K; ++d)
-        for (int j = 0; j < V; ++j) p[j] += S[(size_t)d * V + j] * kt[d];
+      if (!linear)
+        for (int d = 0; d < K; ++d)
+          for (int j = 0; j < V; ++j) p[j] += S[(size_t)d * V + j] * kt[d];
 
       /* write: S <- S + beta_t k_t (v_t - p)^T */
       for (int j = 0; j < V; ++j) p[j] = bt * (vt[j] - p[j]);
@@ -119,4 +127,15 @@ int gdr_oracle_recurrence(int B, int T, int H, int HV, int K, int V,
     free(S); free(p); free(dec);
   }
   return failed ? -2 : 0;
+}
+
+/* The gated delta rule (linear = 0). */
+int gdr_oracle_recurrence(int B, int T, int H, int HV, int K, int V,
+                          int g_per_channel, double scale,
+                          const double* q, const double* k, const double* v,
+                          const double* g, const double* beta,
+                          const double* s0, double* o, double* s_final,
+                          int num_threads) {
+  return gdr_oracle_recurrence_rule(B, T, H, HV, K, V, g_per_channel, 0, scale, q, k, v, g,
+                                    beta, s0, o, s_final, num_threads);
 }

@@ -1,4 +1,5 @@
-"""ctypes wrapper of the fp64 per-token recurrence in gdr_oracle.c.
+"""ctypes wrapper of the fp64 per-token recurrence in gdr_oracle.c (the gated
+delta rule, or the decayed linear attention without the erase term).
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the product path.
@@ -46,6 +47,9 @@ def _load():
         lib.gdr_oracle_recurrence.argtypes = (
             [ctypes.c_int] * 7 + [ctypes.c_double] + [dp] * 8 + [ctypes.c_int])
         lib.gdr_oracle_recurrence.restype = ctypes.c_int
+        lib.gdr_oracle_recurrence_rule.argtypes = (
+            [ctypes.c_int] * 8 + [ctypes.c_double] + [dp] * 8 + [ctypes.c_int])
+        lib.gdr_oracle_recurrence_rule.restype = ctypes.c_int
         lib.gdr_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -66,11 +70,13 @@ def _ptr(x):
 
 
 def recurrence(q, k, v, g, beta, scale: float, s0=None,
-               threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+               threads: int = 0, rule: str = "delta") -> Tuple[np.ndarray, np.ndarray]:
     """Run the fp64 recurrence.
 
     q, k: [B, T, H, K]; v: [B, T, HV, V]; g: [B, T, HV] or [B, T, HV, K];
-    beta: [B, T, HV]; s0: [B, HV, K, V] or None.
+    beta: [B, T, HV]; s0: [B, HV, K, V] or None.  rule "delta" is the gated
+    delta rule; "linear" drops the prediction term (S <- S + beta k v^T, the
+    decayed linear attention of the page's Mamba2 SSD section).
     Returns (o [B, T, HV, V], final_state [B, HV, K, V]) in fp64.
     """
     q, k, v, g, beta, s0 = map(_f64, (q, k, v, g, beta, s0))
@@ -84,8 +90,10 @@ def recurrence(q, k, v, g, beta, scale: float, s0=None,
         assert s0.shape == (B, HV, K, V)
     o = np.empty((B, T, HV, V), np.float64)
     s = np.empty((B, HV, K, V), np.float64)
-    rc = _load().gdr_oracle_recurrence(
-        B, T, H, HV, K, V, int(per_channel), float(scale),
+    if rule not in ("delta", "linear"):
+        raise ValueError(f"unknown rule {rule!r}")
+    rc = _load().gdr_oracle_recurrence_rule(
+        B, T, H, HV, K, V, int(per_channel), int(rule == "linear"), float(scale),
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o),
         _ptr(s), int(threads))
     if rc != 0:
@@ -93,7 +101,8 @@ def recurrence(q, k, v, g, beta, scale: float, s0=None,
     return o, s
 
 
-def recurrence_heads(inp, heads, T: Optional[int] = None, threads: int = 0):
+def recurrence_heads(inp, heads, T: Optional[int] = None, threads: int = 0,
+                     rule: str = "delta"):
     """Recurrence on a subset of (b, hv) pairs of an ``inputs.Inputs``.
 
     Returns {(b, hv): (o [T, V], S [K, V])}.  Used to check full-size runs on
@@ -110,6 +119,6 @@ def recurrence_heads(inp, heads, T: Optional[int] = None, threads: int = 0):
         g = inp.g[b:b + 1, :T, hv:hv + 1]
         be = inp.beta[b:b + 1, :T, hv:hv + 1]
         s0 = None if inp.s0 is None else inp.s0[b:b + 1, hv:hv + 1]
-        o, s = recurrence(q, k, v, g, be, inp.scale, s0, threads)
+        o, s = recurrence(q, k, v, g, be, inp.scale, s0, threads, rule=rule)
         out[(b, hv)] = (o[0, :, 0], s[0, 0])
     return out

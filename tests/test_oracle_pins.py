@@ -346,3 +346,74 @@ def test_l2norm_rows_pins():
     x2[0, 0, 0] *= 7.0
     y2 = l2norm_rows(x2)
     np.testing.assert_array_equal(y2[1:], y[1:])
+
+
+def _masked_attention(q, k, v, g, beta, scale, s0):
+    """Decayed linear attention in its quadratic form (the Mamba2 SSD section
+    of the "Chunkwise parallel algorithms" page, section 1.1: O = ((Q K^T) .
+    Gamma) V, Gamma[t, i] = gamma_t / gamma_i for i <= t), with beta on the
+    columns, the query scale, per-channel decay allowed, and the initial
+    state's decayed contribution; written as dense per-head sums."""
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    G = HV // H
+    o = np.zeros((B, T, HV, V))
+    sT = np.zeros((B, HV, K, V))
+    for b in range(B):
+        for hv in range(HV):
+            h = hv // G
+            gg = g[b, :, hv] if g.ndim == 4 else np.repeat(g[b, :, hv][:, None], K, 1)
+            Gam = np.cumsum(gg, axis=0)                     # [T, K], inclusive
+            for t in range(T):
+                for i in range(t + 1):
+                    w = (q[b, t, h] * np.exp(Gam[t] - Gam[i]) * k[b, i, h]).sum()
+                    o[b, t, hv] += scale * beta[b, i, hv] * w * v[b, i, hv]
+                if s0 is not None:
+                    o[b, t, hv] += scale * (q[b, t, h] * np.exp(Gam[t])) @ s0[b, hv]
+            for i in range(T):
+                sT[b, hv] += beta[b, i, hv] * np.outer(np.exp(Gam[T - 1] - Gam[i]) * k[b, i, h],
+                                                      v[b, i, hv])
+            if s0 is not None:
+                sT[b, hv] += np.exp(Gam[T - 1])[:, None] * s0[b, hv]
+    return o, sT
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_linear_rule_equals_masked_attention(per_channel):
+    """The linear rule (no erase) equals the quadratic masked-attention form,
+    o and final state, with grouped heads and an initial state."""
+    rng = np.random.default_rng(11)
+    B, T, H, HV, K, V = 1, 23, 1, 2, 5, 3
+    q, k = rng.standard_normal((2, B, T, H, K))
+    v = rng.standard_normal((B, T, HV, V))
+    beta = rng.uniform(0.1, 1.0, (B, T, HV))
+    g = -rng.uniform(0.0, 0.5, (B, T, HV, K) if per_channel else (B, T, HV))
+    s0 = rng.standard_normal((B, HV, K, V))
+    o, s = oracle.recurrence(q, k, v, g, beta, 0.7, s0, rule="linear")
+    ro, rs = _masked_attention(q, k, v, g, beta, 0.7, s0)
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s, rs, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_rule_page_form_and_delta_difference():
+    """beta = 1, scale = 1, zero state: exactly the page's O = ((Q K^T) . Gamma) V;
+    and the delta rule differs from it as soon as a key meets the state."""
+    rng = np.random.default_rng(12)
+    B, T, H, K, V = 1, 9, 1, 4, 4
+    q, k = rng.standard_normal((2, B, T, H, K))
+    v = rng.standard_normal((B, T, H, V))
+    g = np.log(rng.uniform(0.5, 1.0, (B, T, H)))
+    one = np.ones((B, T, H))
+    o, _ = oracle.recurrence(q, k, v, g, one, 1.0, None, rule="linear")
+    gam = np.exp(np.cumsum(g[0, :, 0]))
+    Gmask = np.tril(gam[:, None] / gam[None, :])
+    page = ((q[0, :, 0] @ k[0, :, 0].T) * Gmask) @ v[0, :, 0]
+    np.testing.assert_allclose(o[0, :, 0], page, rtol=1e-12, atol=1e-12)
+    od, _ = oracle.recurrence(q, k, v, g, one, 1.0, None)
+    assert np.abs(od - o).max() > 1e-3
+    # with one token from a zero state the two rules coincide
+    o1, s1 = oracle.recurrence(q[:, :1], k[:, :1], v[:, :1], g[:, :1], one[:, :1], 1.0, None,
+                               rule="linear")
+    o2, s2 = oracle.recurrence(q[:, :1], k[:, :1], v[:, :1], g[:, :1], one[:, :1], 1.0, None)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
