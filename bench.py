@@ -98,7 +98,7 @@ def measured_traffic(w, stage_kernels):
     return total if found else None
 
 
-def cpu_baseline(inp, budget_s):
+def cpu_baseline(inp, budget_s, rule="delta"):
     import oracle
     w = inp.w
     threads = min(os.cpu_count() or 1, w.B * w.HV)
@@ -108,7 +108,7 @@ def cpu_baseline(inp, budget_s):
     t0 = time.perf_counter()
     oracle.recurrence(inp.q[:, :probe_T], inp.k[:, :probe_T], inp.v[:, :probe_T],
                       inp.g[:, :probe_T], inp.beta[:, :probe_T], inp.scale,
-                      inp.s0, threads=threads)
+                      inp.s0, threads=threads, rule=rule)
     rate = probe_T / max(time.perf_counter() - t0, 1e-9)     # token positions / s
     if w.T / rate > budget_s:
         Ts = max(probe_T, int(rate * budget_s))
@@ -116,11 +116,11 @@ def cpu_baseline(inp, budget_s):
     while spent < budget_s * 0.5 or reps == 0:
         t0 = time.perf_counter()
         oracle.recurrence(inp.q[:, :Ts], inp.k[:, :Ts], inp.v[:, :Ts], inp.g[:, :Ts],
-                          inp.beta[:, :Ts], inp.scale, inp.s0, threads=threads)
+                          inp.beta[:, :Ts], inp.scale, inp.s0, threads=threads, rule=rule)
         spent += time.perf_counter() - t0
         tokens += w.B * Ts
         reps += 1
-    sample = (f"fp64 recurrence on all {w.B * w.HV} (batch, value head) scans, "
+    sample = (f"fp64 {rule}-rule recurrence on all {w.B * w.HV} (batch, value head) scans, "
               f"{'all' if Ts == w.T else 'first'} {Ts} of {w.T} tokens, x{reps} passes, "
               f"{spent:.1f} s")
     return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -164,7 +164,7 @@ def bench_decode(args, w, inp):
 
     def step(d):
         gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s"], scale=inp.scale,
-                            out=(d["o"], d["s"]), slab=args.slab)
+                            out=(d["o"], d["s"]), slab=args.slab, rule=args.rule)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -204,7 +204,7 @@ def bench_decode(args, w, inp):
         "config": {"workload": w.name, "B": w.B, "T": 1, "H": w.H, "HV": w.HV, "K": w.K,
                    "V": w.V, "decay": "per-channel" if w.per_channel else "scalar",
                    "inputs": w.dtype, "state": "fp32, updated in place",
-                   "columns_per_workgroup": args.slab or "auto",
+                   "columns_per_workgroup": args.slab or "auto", "rule": args.rule,
                    "rotating_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -213,7 +213,7 @@ def bench_decode(args, w, inp):
                      "algorithmic_bytes": nbytes, "kernel_ms": {"decode_step": kernel_ms}},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule)
     print(json.dumps(rec), flush=True)
 
 
@@ -245,6 +245,9 @@ def main():
     ap.add_argument("--slab", type=int, default=0, choices=(0, 32, 64, 128),
                     help="state columns per scan (32, 64) or decode (32, 64, 128) "
                          "workgroup (0: the library's choice)")
+    ap.add_argument("--rule", default="delta", choices=("delta", "linear"),
+                    help="state update: gated delta rule, or decayed linear attention "
+                         "(no erase term)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -286,8 +289,8 @@ def main():
                 s0=None if inp.s0 is None else to_dev(inp.s0))
     prob = gdr.problem(w.B, w.T, w.H, w.HV, w.K, w.V, chunk=w.chunk,
                        per_channel=w.per_channel, scale=inp.scale, dtype=w.dtype,
-                       segments=args.segments, slab=args.slab)
-    knobs = dict(segments=args.segments, slab=args.slab)
+                       segments=args.segments, slab=args.slab, rule=args.rule)
+    knobs = dict(segments=args.segments, slab=args.slab, rule=args.rule)
     ws_bytes = gdr.workspace_size(prob)
     per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
     per_set += ws_bytes + w.B * w.T * w.HV * w.V * 4 + w.B * w.HV * w.K * w.V * 4
@@ -397,7 +400,7 @@ def main():
                    "V": w.V, "chunk": w.chunk,
                    "decay": "per-channel" if w.per_channel else "scalar",
                    "inputs": w.dtype, "initial_state": w.s0_std > 0,
-                   "accumulate": "fp32", "rotating_sets": nsets},
+                   "accumulate": "fp32", "rotating_sets": nsets, "rule": args.rule},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
                      "kernels": list(dom_kernels), "algorithmic_bytes": dom_bytes,
@@ -410,7 +413,7 @@ def main():
         "fwd_entry_point_matches": same,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule)
     print(json.dumps(rec), flush=True)
 
 

@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdr.so")
 
 GDR_F32, GDR_BF16 = 0, 1
+RULES = {"delta": 0, "linear": 1}   # gdr_rule: gated delta rule, decayed linear attention
 GDR_OK = 0
 STATUS_NAMES = {
     0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_SHAPE", 3: "GDR_ERR_DTYPE",
@@ -33,7 +34,7 @@ class GdrProblem(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("g_per_channel", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32),
                 ("scan_segments", ctypes.c_int32), ("scan_slab", ctypes.c_int32),
-                ("qk_l2norm", ctypes.c_int32)]
+                ("qk_l2norm", ctypes.c_int32), ("rule", ctypes.c_int32)]
 
 
 class GdrError(RuntimeError):
@@ -91,11 +92,11 @@ def check(status: int) -> None:
 def problem(B: int, T: int, H: int, HV: int, K: int, V: int, *, chunk: int = 64,
             per_channel: bool = False, scale: Optional[float] = None,
             dtype: str = "bf16", segments: int = 0, slab: int = 0,
-            qk_l2norm: bool = False) -> GdrProblem:
+            qk_l2norm: bool = False, rule: str = "delta") -> GdrProblem:
     return GdrProblem(B, T, H, HV, K, V, chunk, int(bool(per_channel)),
                       float(K ** -0.5 if scale is None else scale),
                       {"fp32": GDR_F32, "bf16": GDR_BF16}[dtype], int(segments), int(slab),
-                      int(bool(qk_l2norm)))
+                      int(bool(qk_l2norm)), RULES[rule])
 
 
 def scan_segments(prob: GdrProblem) -> int:
@@ -117,7 +118,7 @@ def _ptr(t) -> Optional[int]:
 
 
 def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
-                  qk_l2norm=False) -> GdrProblem:
+                  qk_l2norm=False, rule="delta") -> GdrProblem:
     import torch
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
@@ -146,7 +147,7 @@ def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
             raise TypeError(f"{name} must be float32")
     return problem(B, T, H, HV, K, V, chunk=chunk, per_channel=per_channel, scale=scale,
                    dtype="fp32" if q.dtype == torch.float32 else "bf16", segments=segments,
-                   slab=slab, qk_l2norm=qk_l2norm)
+                   slab=slab, qk_l2norm=qk_l2norm, rule=rule)
 
 
 def _check_tensors(dev, **ts):
@@ -167,7 +168,7 @@ def _stream(dev) -> ctypes.c_void_p:
 def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
                   scale: Optional[float] = None, *, output_final_state: bool = True,
                   workspace=None, out=None, segments: int = 0, slab: int = 0,
-                  qk_l2norm: bool = False
+                  qk_l2norm: bool = False, rule: str = "delta"
                   ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunkwise gated delta rule forward on the GPU.
 
@@ -179,13 +180,15 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     may be passed to avoid allocations.  ``segments`` > 0 asks for that many
     sequence segments in the state scan (0: automatic); ``slab`` (32 or 64)
     sets the state columns per scan workgroup (0: automatic).  ``qk_l2norm``
-    L2-normalises every q and k row inside the kernels first.
+    L2-normalises every q and k row inside the kernels first.  ``rule`` is
+    "delta" (the gated delta rule) or "linear" (decayed linear attention,
+    no erase term).
     """
     import torch
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if initial_state is not None and (initial_state.dtype != torch.float32 or
@@ -212,7 +215,7 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
 def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None, *,
                    V: Optional[int] = None, inspect: bool = False,
                    workspace=None, segments: int = 0, slab: int = 0,
-                   qk_l2norm: bool = False
+                   qk_l2norm: bool = False, rule: str = "delta"
                    ) -> Tuple["torch.Tensor", Dict[str, "torch.Tensor"]]:
     """Run the chunk-preparation stage alone.
 
@@ -223,7 +226,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, g=g, beta=beta)
-    prob = _problem_from(q, k, None, g, beta, chunk, scale, segments, slab, qk_l2norm)
+    prob = _problem_from(q, k, None, g, beta, chunk, scale, segments, slab, qk_l2norm, rule)
     if V is not None:
         prob.V = V
     nbytes = workspace_size(prob)
@@ -249,7 +252,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
 
 def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 64,
                    scale: Optional[float] = None, *, out=None, segments: int = 0,
-                   slab: int = 0, qk_l2norm: bool = False):
+                   slab: int = 0, qk_l2norm: bool = False, rule: str = "delta"):
     """Run the state-scan stage on a workspace filled by gdr_chunk_prep.
 
     ``out`` = (o, final_state) reuses caller tensors (final_state may be None).
@@ -258,7 +261,7 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if out is not None:
@@ -273,8 +276,8 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
 
 
 def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None, *,
-                    out=None, inplace: bool = False, slab: int = 0, qk_l2norm: bool = False
-                    ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+                    out=None, inplace: bool = False, slab: int = 0, qk_l2norm: bool = False,
+                    rule: str = "delta") -> Tuple["torch.Tensor", "torch.Tensor"]:
     """One decode step (one token per sequence) on the GPU.
 
     q, k: [B, H, K]; v: [B, HV, V] (float32 or bfloat16, one dtype);
@@ -284,7 +287,7 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     With ``inplace`` the new state overwrites ``state``; ``out`` = (o, S) may
     be passed to avoid allocations.  ``slab`` (32, 64 or 128) sets the state
     columns per workgroup (0: automatic).  ``qk_l2norm`` L2-normalises q and
-    k inside the kernel first.
+    k inside the kernel first; ``rule`` "linear" drops the erase term.
     """
     import torch
     lib = load()
@@ -317,7 +320,7 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
         raise ValueError("inplace needs a state")
     prob = problem(B, 1, H, HV, K, V, per_channel=per_channel, scale=scale,
                    dtype="fp32" if q.dtype == torch.float32 else "bf16", slab=slab,
-                   qk_l2norm=qk_l2norm)
+                   qk_l2norm=qk_l2norm, rule=rule)
     if out is not None:
         o, s = out
     else:

@@ -28,6 +28,7 @@ struct Prob {
   int nseg, seg_len; // sequence segments of the state scan
   int bv;            // state columns per scan workgroup (32 or 64)
   bool l2norm;       // L2-normalise the q and k rows in the prep kernels
+  bool linear;       // decayed linear attention (no erase term)
 };
 
 // Number of sequence segments for the state scan.  One segment runs the
@@ -75,6 +76,7 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
   if (p->g_per_channel != 0 && p->g_per_channel != 1) return GDR_ERR_ARG;
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDR_ERR_ARG;
+  if (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) return GDR_ERR_ARG;
   if (!std::isfinite(p->scale)) return GDR_ERR_ARG;
   if (p->chunk != kChunk) return GDR_ERR_UNSUPPORTED;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
@@ -85,6 +87,7 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.f32 = p->qkv_dtype == GDR_F32;
   r.scale = p->scale;
   r.l2norm = p->qk_l2norm == 1;
+  r.linear = p->rule == GDR_RULE_LINEAR;
   r.es = r.f32 ? 4 : 2;
   if (p->scan_segments < 0) return GDR_ERR_ARG;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
@@ -256,6 +259,7 @@ PrepArgs prep_args(const Prob& r, const void* q, const void* k, const float* g,
   a.wt = base + L.wt; a.ah = base + L.ah; a.rs = reinterpret_cast<float*>(base + L.rs);
   a.qh = base + L.qh; a.kh = base + L.kh;
   a.l2norm = r.l2norm ? 1 : 0;
+  a.linear = r.linear ? 1 : 0;
   a.d_gamma = a.d_akk = a.d_aqk = a.d_minv = nullptr;
   return a;
 }
@@ -271,6 +275,7 @@ ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
   a.B = r.B; a.T = r.T; a.H = r.H; a.HV = r.HV; a.N = r.N;
   a.scale = r.scale;
   a.seg_len = r.seg_len; a.nseg = r.nseg;
+  a.linear = r.linear ? 1 : 0;
   a.phi = base + L.phi;
   a.eend = reinterpret_cast<float*>(base + L.eend);
   return a;
@@ -325,7 +330,8 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
     return GDR_ERR_SHAPE;
   if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
   if ((p->g_per_channel != 0 && p->g_per_channel != 1) ||
-      (p->qk_l2norm != 0 && p->qk_l2norm != 1) || !std::isfinite(p->scale))
+      (p->qk_l2norm != 0 && p->qk_l2norm != 1) ||
+      (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) || !std::isfinite(p->scale))
     return GDR_ERR_ARG;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64 && p->scan_slab != 128)
@@ -356,6 +362,7 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   a.B = p->B; a.H = p->H; a.HV = p->HV;
   a.scale = p->scale;
   a.l2norm = p->qk_l2norm;
+  a.linear = p->rule == GDR_RULE_LINEAR;
   const bool f32 = p->qkv_dtype == GDR_F32;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int vb = decode_columns(p);
@@ -465,7 +472,7 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace NULL or smaller than gdr_chunk_fwd_workspace_size";
     case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE: the current HIP device is not gfx950";
     case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP query or kernel launch failed";
-    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel and qk_l2norm 0 or 1, scan_segments >= 0, scan_slab 0, 32 or 64 (128 for decode)";
+    case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel and qk_l2norm 0 or 1, rule a gdr_rule, scan_segments >= 0, scan_slab 0, 32 or 64 (128 for decode)";
     case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: an output overlaps an input or another output";
     default: return "GDR_ERR_UNKNOWN: unknown status value";
   }

@@ -9,7 +9,9 @@
 //   o  = scale S'^T q = scale ((diag(d) S)^T q + beta u (q . k))
 //
 // optionally with q and k L2-normalised first (x rsqrt(sum x^2 + 1e-6)),
-// which the kernel applies as factors on the raw rows' sums, in fp32.
+// which the kernel applies as factors on the raw rows' sums, in fp32; or,
+// for the decayed linear attention (the page's Mamba2 SSD section), with
+// u = v: no erase term.
 //
 // The step reads and writes the K x V fp32 state once; every other operand is
 // a vector, so the kernel is bound by HBM bandwidth on the state.  The
@@ -39,6 +41,7 @@ struct DecodeArgs {
   int B, H, HV;
   float scale;
   int l2norm;            // 1: L2-normalise q and k first
+  int linear;            // 1: decayed linear attention: u = v (no erase term)
 };
 
 template <class T>
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   Bq = srq * (sB[0][c4] + sB[1][c4] + sB[2][c4] + sB[3][c4]);
   const float bt = a.beta[bh];
   const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * c4);
-  const f32x4 u = vv - A;
+  const f32x4 u = a.linear ? vv : vv - A;
   if (wave == 0 && lane < LPR)
     *reinterpret_cast<f32x4*>(a.o + (size_t)bh * V + v0 + 4 * c4) =
         a.scale * (Bq + (bt * sqk) * u);

@@ -40,6 +40,7 @@ struct PrepArgs {
   void* qh;
   void* kh;
   int l2norm;      // 1: L2-normalise every q and k row first
+  int linear;      // 1: decayed linear attention (no erase term): A_kk = 0, M = I
   float* d_gamma;  // optional inspection outputs (fp32)
   float* d_akk;
   float* d_aqk;
@@ -260,7 +261,7 @@ template <int W, int K, class P>
 __device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typename P::in_t* sQ,
                                            float* sL, const float* sGam, const float* sBeta,
                                            const float* sRq, const float* sRk, float scale,
-                                           int r, int grp, f32x4 (&aqT)[4]) {
+                                           bool linear, int r, int grp, f32x4 (&aqT)[4]) {
   using in_t = typename P::in_t;
   using gfrag_t = std::conditional_t<P::kF32, f32x8, bf16x8>;
   constexpr int KB = K / 32;
@@ -328,7 +329,9 @@ __device__ __forceinline__ void gram_tiles(const typename P::in_t* sK, const typ
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const float x = acc[j4] * b1[Y] * rk4[X][j4] * __expf(g4[X][j4] - g1[Y]);
-        sL[(16 * X + 4 * grp + j4) * LP + 16 * Y + r] = (X > Y || 4 * grp + j4 > r) ? x : 0.f;
+        // (the linear rule has no erase term: M = I)
+        sL[(16 * X + 4 * grp + j4) * LP + 16 * Y + r] =
+            ((X > Y || 4 * grp + j4 > r) && !linear) ? x : 0.f;
       }
     }
     if constexpr (j < 4) {
@@ -487,10 +490,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) aqT[j] = zero4();
   switch (wave) {
-    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
-    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
-    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
-    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale, r, grp, aqT); break;
+    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
   }
 
   lds_barrier();   // sL complete

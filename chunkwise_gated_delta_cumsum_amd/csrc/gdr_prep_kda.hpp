@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const int ii = 16 * I + 4 * grp + j4, jj = 16 * J + r;
-        sL[ii * LP + jj] = akk[j4] * sBeta[jj];
+        sL[ii * LP + jj] = a.linear ? 0.f : akk[j4] * sBeta[jj];   // linear rule: M = I
         aq[j4] *= sBeta[16 * J + 4 * grp + j4] * a.scale;
       }
       aqT[J] = aq;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
 #pragma unroll
   for (int j4 = 0; j4 < 4; ++j4) {
     const int rr = 16 * I + 4 * grp + j4, cc = 16 * I + r;
-    sL[rr * LP + cc] = rr > cc ? dkk[j4] * sBeta[cc] : 0.f;
+    sL[rr * LP + cc] = (rr > cc && !a.linear) ? dkk[j4] * sBeta[cc] : 0.f;
     aqT[I][j4] = rr <= cc ? dqk[j4] * sBeta[rr] * a.scale : 0.f;
   }
 

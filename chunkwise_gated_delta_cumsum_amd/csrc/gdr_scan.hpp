@@ -7,7 +7,9 @@
 //   o = exp(gamma) scale q S + A^ Z             (= (q exp(gamma)) S + A_qk r)
 //   S <- diag(exp(gamma_last)) S + W^T Z        (= ... + K~^T diag(beta) r)
 // (per-channel decay: the prep kernel folds exp(gamma) into the q, k
-// fragments, so the row scales are 1.)
+// fragments, so the row scales are 1.)  For the decayed linear attention
+// (no erase term) M = I, so W^ = diag(beta exp(gamma_last - gamma)) k and
+// A^ = A_qk, and Z = v: the same loop with the prediction dropped.
 //
 // The state update is affine in S: S_{n+1} = A_n S_n + B_n.  A sequence cut
 // into segments is therefore run in two passes:
@@ -69,6 +71,7 @@ struct ScanArgs {
   const void* kh;
   int B, T, H, HV, N;
   float scale;
+  int linear;        // 1: decayed linear attention: Z = v (no prediction term)
   // segment p covers chunks [p * seg_len, min((p + 1) * seg_len, N))
   int seg_len, nseg;
   void* phi;         // transitions [BH][nseg-1], each K x K in A-fragment order
@@ -497,9 +500,9 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
           const float vv =
               PHI ? 0.f : P::in_to_f32(sVw[(16 * c2 + 4 * grp + j) * VP + 16 * ct + r]);
           if constexpr (PERCH)
-            z[c2][j] = vv - Y[c2][ct][j];
+            z[c2][j] = a.linear ? vv : vv - Y[c2][ct][j];
           else
-            z[c2][j] = vv - cur.eg[c2][j] * Y[c2][ct][j];
+            z[c2][j] = a.linear ? vv : vv - cur.eg[c2][j] * Y[c2][ct][j];
         }
 #pragma unroll
       for (int c2 = 0; c2 < CT; ++c2) {

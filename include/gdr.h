@@ -69,6 +69,7 @@ typedef enum gdr_status {
   GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
   GDR_ERR_HIP = 8,         /* a HIP query or kernel launch failed */
   GDR_ERR_ARG = 9,         /* scale not finite, g_per_channel or qk_l2norm not 0/1,
+                              rule not a gdr_rule,
                               scan_segments < 0, or scan_slab not 0, 32 or 64
                               (gdr_decode_step also takes 128) */
   GDR_ERR_ALIAS = 10       /* an output overlaps an input or the other output
@@ -76,6 +77,16 @@ typedef enum gdr_status {
 } gdr_status;
 
 typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* The state update.  GDR_RULE_DELTA is the gated delta rule above.
+ * GDR_RULE_LINEAR drops its prediction (erase) term,
+ *     S <- diag(exp(g_t)) S + beta_t k_t v_t^T,  o_t = scale * S^T q_t,
+ * the decayed linear attention of the Mamba2 state-space-duality section of
+ * the "Chunkwise parallel algorithms" page (section 1.1; beta = 1 and
+ * scale = 1 give its form exactly; per-channel g gives the gated linear
+ * attention form).  Its chunk form is the same with M = I: the UT transform
+ * drops out. */
+typedef enum gdr_rule { GDR_RULE_DELTA = 0, GDR_RULE_LINEAR = 1 } gdr_rule;
 
 typedef struct gdr_problem {
   int32_t B, T, H, HV, K, V; /* batch, tokens, q/k heads, value heads, key dim, value dim */
@@ -98,6 +109,7 @@ typedef struct gdr_problem {
                                 multiplies its raw values in fp32 wherever
                                 they enter a product.  0: q and k are used as
                                 given */
+  int32_t rule;              /* gdr_rule: GDR_RULE_DELTA (0) or GDR_RULE_LINEAR */
 } gdr_problem;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when

@@ -232,3 +232,14 @@ def test_qk_l2norm_flag_validation(lib):
     assert binding.STATUS_NAMES[call_decode(lib, bad1)] == "GDR_ERR_ARG"
     ok = base(T=100, qk_l2norm=True)
     assert ok.qk_l2norm == 1 and gdr.workspace_size(ok) == gdr.workspace_size(base(T=100))
+
+
+def test_rule_validation(lib):
+    bad = base(T=100)
+    bad.rule = 2
+    assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"
+    bad1 = base(T=1)
+    bad1.rule = -1
+    assert binding.STATUS_NAMES[call_decode(lib, bad1)] == "GDR_ERR_ARG"
+    lin = base(T=100, rule="linear")
+    assert lin.rule == 1 and gdr.workspace_size(lin) == gdr.workspace_size(base(T=100))
