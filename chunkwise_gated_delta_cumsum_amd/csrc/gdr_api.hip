@@ -225,8 +225,28 @@ gdr_status launch_scan_kvb(const Prob& r, ScanArgs& a, hipStream_t s) {
                 grid_for(BH * r.nseg, V / BV), kScanWaves * 64, a, s);
 }
 
+// The linear rule with 64-column slabs runs its own instantiation (no Y, one
+// barrier per chunk step); with 32-column slabs it takes the general kernels,
+// which drop the prediction term at run time.
+template <int K, int V, bool PERCH, class P>
+gdr_status launch_scan_lin(const Prob& r, ScanArgs& a, hipStream_t s) {
+  const size_t BH = (size_t)r.B * r.HV;
+  auto grid_for = [](size_t units, int nslab) {
+    return (unsigned)((units + 7) / 8 * 8 * nslab);
+  };
+  gdr_status st;
+  if (r.nseg > 1) {
+    st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain, 64, true>,
+                grid_for(BH * (r.nseg - 1), (K + V) / 64), kScanWaves * 64, a, s);
+    if (st != GDR_OK) return st;
+  }
+  return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, 64, true>,
+                grid_for(BH * r.nseg, V / 64), kScanWaves * 64, a, s);
+}
+
 template <int K, int V, bool PERCH, class P>
 gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
+  if (r.linear && r.bv == 64) return launch_scan_lin<K, V, PERCH, P>(r, a, s);
   return r.bv == 32 ? launch_scan_kvb<K, V, PERCH, P, 32>(r, a, s)
                     : launch_scan_kvb<K, V, PERCH, P, 64>(r, a, s);
 }

@@ -223,7 +223,7 @@ __device__ __forceinline__ void combine_prefix(const ScanArgs& a, typename P::fr
 // One wave of a scan workgroup.  W (the wave index) and PHI (chain mode:
 // transition slab, identity start and no v) are template arguments so that
 // every choice between waves and slab kinds folds at compile time.
-template <int K, int V, bool PERCH, class P, int MODE, int BV, int NW, int W, bool PHI>
+template <int K, int V, bool PERCH, class P, int MODE, int BV, int NW, int W, bool PHI, bool LIN>
 __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t* sS,
                                           typename P::frag_t* sZ, typename P::in_t* sVw,
                                           unsigned char* stg, int unit, int sv) {
@@ -309,9 +309,9 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   // the wave at issue (in order) while the memory pipeline drains it.
   constexpr int NKQ = CT * KB;                  // load items per k / q operand
   constexpr int IT_K = 0;
-  constexpr int IT_Q = IT_K + NKQ;
+  constexpr int IT_Q = IT_K + (LIN ? 0 : NKQ);  // the linear rule never reads k here
   constexpr int IT_W = IT_Q + (FULL ? NKQ : 0);
-  constexpr int IT_A = IT_W + SRT * 2;
+  constexpr int IT_A = IT_W + ((LIN && PHI) ? 0 : SRT * 2);
   constexpr int IT_R = IT_A + (FULL ? CT * AKB : 0);
   constexpr int NITEMS = IT_R + 1;
   auto load_item = [&](int i, int n, WA& x) {
@@ -396,8 +396,29 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
       }
     }
   };
+  // The linear rule (LIN): Z = v does not depend on the state, so the v rows
+  // of a chunk go to the Z fragments at the end of the step before it (two
+  // alternating buffers), and the barrier at the top of the step publishes
+  // them with the state: one barrier per step instead of two, and no Y.
+  auto publish_vz = [&](int n) {
+    if constexpr (LIN && !PHI) {
+      frag_t* zb = sZ + (n & 1) * (2 * NCT * 64);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int c2 = 0; c2 < CT; ++c2) {
+          f32x4 z;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            z[j] = P::in_to_f32(sVw[(16 * c2 + 4 * grp + j) * VP + 16 * ct + r]);
+          const int tile = CT * w + c2;
+          store_half(&zb[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, z);
+        }
+    }
+  };
   load_v(n0);
   stage_v();
+  publish_vz(n0);
 
   // o^T of a chunk leaves at the end of its step, after its last product and
   // after every load of the step is issued (so that no later wait for those
@@ -435,13 +456,21 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     GDR_PROF(0);
     // the next chunk's v (into the LDS tile at the end of this step)
     if constexpr (!PHI) load_v(nn);
-    // this wave's state rows as halves of the B fragments of S
+    // this wave's state rows as halves of the B fragments of S (the linear
+    // rule's chain pass reads no state across waves: no Y and no o).  With
+    // one barrier per step (LIN) a wave may still read the state of the step
+    // before while another writes this one, so S alternates between two
+    // buffers as Z does; the barrier of step n orders the reads of step n-1
+    // before the writes of step n + 1 to the same buffer.
+    frag_t* sSb = LIN ? sS + (n & 1) * (KB * NCT * 64) : sS;
+    if constexpr (!(LIN && !FULL)) {
 #pragma unroll
-    for (int st = 0; st < SRT; ++st) {
-      const int tile = SRT * w + st;
+      for (int st = 0; st < SRT; ++st) {
+        const int tile = SRT * w + st;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        store_half(&sS[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
+        for (int ct = 0; ct < NCT; ++ct)
+          store_half(&sSb[((tile >> 1) * NCT + ct) * 64 + lane], tile & 1, S[st][ct]);
+      }
     }
     GDR_PROF(11);
     lds_barrier();
@@ -459,27 +488,27 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
         Y[c2][ct] = zero4();
         OT[ct][c2] = zero4();
       }
-    {
+    if constexpr (!(LIN && !FULL)) {
       // every B fragment of S at once, so the LDS latency is paid once
       frag_t bS[KB][NCT];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) bS[kb][ct] = sS[(kb * NCT + ct) * 64 + lane];
+        for (int ct = 0; ct < NCT; ++ct) bS[kb][ct] = sSb[(kb * NCT + ct) * 64 + lane];
       GDR_PROF(7);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         frag_t fk[CT], fq[CT];
 #pragma unroll
         for (int c2 = 0; c2 < CT; ++c2) {
-          fk[c2] = cur.kf[c2][kb];
+          if constexpr (!LIN) fk[c2] = cur.kf[c2][kb];
           if constexpr (FULL) fq[c2] = cur.qf[c2][kb];
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
           for (int c2 = 0; c2 < CT; ++c2) {
-            Y[c2][ct] = mma32(fk[c2], bS[kb][ct], Y[c2][ct]);
+            if constexpr (!LIN) Y[c2][ct] = mma32(fk[c2], bS[kb][ct], Y[c2][ct]);
             if constexpr (FULL) OT[ct][c2] = mma32(bS[kb][ct], fq[c2], OT[ct][c2]);
           }
           if (item < NITEMS) load_item(item++, nn, nxt);
@@ -490,6 +519,8 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     GDR_PROF(2);
 
     // Z = v - exp(gamma) Y, published as halves of the B fragments of Z
+    // (the linear rule published Z = v at the end of the step before)
+    if constexpr (!LIN) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 z[CT];
@@ -511,6 +542,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
       }
     }
     lds_barrier();
+    }
     GDR_PROF(3);
 
     // S <- diag(exp(gamma_last)) S + W^T Z, and o^T = exp(gamma) scale o^T + Z^T A^T
@@ -518,23 +550,31 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
 #pragma unroll
     for (int c2 = 0; c2 < CT; ++c2) sc[c2] = (FULL && !PERCH) ? cur.ego[c2] * a.scale : 1.f;
     frag_t bZ[2][NCT];
+    const frag_t* zr = LIN ? sZ + (n & 1) * (2 * NCT * 64) : sZ;
+    if constexpr (!(LIN && PHI)) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      bZ[0][ct] = sZ[(0 * NCT + ct) * 64 + lane];
-      bZ[1][ct] = sZ[(1 * NCT + ct) * 64 + lane];
+      for (int ct = 0; ct < NCT; ++ct) {
+        bZ[0][ct] = zr[(0 * NCT + ct) * 64 + lane];
+        bZ[1][ct] = zr[(1 * NCT + ct) * 64 + lane];
+      }
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const frag_t z0 = bZ[0][ct];
-      const frag_t z1 = bZ[1][ct];
+      frag_t z0 = {}, z1 = {};
+      if constexpr (!(LIN && PHI)) {
+        z0 = bZ[0][ct];
+        z1 = bZ[1][ct];
+      }
 #pragma unroll
       for (int st = 0; st < SRT; ++st) {
         if constexpr (PERCH)
           S[st][ct] *= cur.dl[st];
         else
           S[st][ct] *= cur.dl[0][0];
-        S[st][ct] = mma32(cur.wf[st][0], z0, S[st][ct]);
-        S[st][ct] = mma32(cur.wf[st][1], z1, S[st][ct]);
+        if constexpr (!(LIN && PHI)) {   // (the linear rule's transition: Z = 0)
+          S[st][ct] = mma32(cur.wf[st][0], z0, S[st][ct]);
+          S[st][ct] = mma32(cur.wf[st][1], z1, S[st][ct]);
+        }
         if (item < NITEMS) load_item(item++, nn, nxt);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -558,6 +598,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
       store_o(n);
     }
     stage_v();
+    publish_vz(n + 1);
     GDR_PROF(4);
 
     GDR_PROF(5);
@@ -616,7 +657,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   }
 }
 
-template <int K, int V, bool PERCH, class P, int MODE, int BV>
+template <int K, int V, bool PERCH, class P, int MODE, int BV, bool LIN = false>
 __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
@@ -627,8 +668,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   constexpr int KB = K / 32;
   constexpr int VVEC = 16 / (int)sizeof(in_t);
   constexpr int VP = BV + VVEC;
-  __shared__ frag_t sS[KB * NCT * 64];                // B fragments of S
-  __shared__ frag_t sZ[2 * NCT * 64];                 // B fragments of Z
+  __shared__ frag_t sS[(LIN ? 2 : 1) * KB * NCT * 64];  // B fragments of S (2 buffers: LIN)
+  __shared__ frag_t sZ[(LIN ? 2 : 1) * 2 * NCT * 64];  // B fragments of Z (2 buffers: LIN)
   __shared__ __attribute__((aligned(16))) in_t sV[NW][(64 / NW) * VP];
   __shared__ __attribute__((aligned(16))) unsigned char sStg[NW][scan_stage_bytes<MODE, BV>()];
 
@@ -639,12 +680,12 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   GDR_WGT(FULL ? 3 : 1, 0);
   auto run = [&](auto phi) {
     constexpr bool PHI = decltype(phi)::value;
-    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, BV, NW, 0, PHI>(a, sS, sZ, sV[0], sStg[0], unit, sv);
+    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, BV, NW, 0, PHI, LIN>(a, sS, sZ, sV[0], sStg[0], unit, sv);
     if constexpr (NW > 1)
-      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, BV, NW, 1, PHI>(a, sS, sZ, sV[1], sStg[1], unit, sv);
+      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, BV, NW, 1, PHI, LIN>(a, sS, sZ, sV[1], sStg[1], unit, sv);
     if constexpr (NW > 2) {
-      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, BV, NW, 2, PHI>(a, sS, sZ, sV[2], sStg[2], unit, sv);
-      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, BV, NW, 3, PHI>(a, sS, sZ, sV[3], sStg[3], unit, sv);
+      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, BV, NW, 2, PHI, LIN>(a, sS, sZ, sV[2], sStg[2], unit, sv);
+      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, BV, NW, 3, PHI, LIN>(a, sS, sZ, sV[3], sStg[3], unit, sv);
     }
   };
   if (FULL || sv >= K / BV)
