@@ -9,4 +9,4 @@ from .binding import (GDR_BF16, GDR_F32, EXPORTED, GdrError, GdrProblem, LIB_PAT
                       problem,
                       scan_segments, scan_slab, status_string, workspace_size)
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

@@ -510,6 +510,6 @@ int gdr_chunk_scan_slab(const gdr_problem* p) {
   return r.bv;
 }
 
-int gdr_version(void) { return 100; }
+int gdr_version(void) { return 200; }   // 0.2.0: gdr_problem gained scan_slab, qk_l2norm and rule
 
 }  // extern "C"

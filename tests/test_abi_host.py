@@ -50,7 +50,14 @@ def test_status_strings(lib):
     for code, name in binding.STATUS_NAMES.items():
         assert gdr.status_string(code).startswith(name)
     assert gdr.status_string(12345).startswith("GDR_ERR_UNKNOWN")
-    assert lib.gdr_version() >= 100
+    assert lib.gdr_version() >= 200
+    # the binding's struct must match the header's field for field
+    import re as _re
+    body = open(HEADER).read().split("typedef struct gdr_problem {")[1].split("} gdr_problem;")[0]
+    body = _re.sub(r"/\*.*?\*/", "", body, flags=_re.S)
+    names = [n for decl in body.split(";") for n in _re.findall(r"\b(\w+)\s*(?:,|$)", decl.strip())
+             if n not in ("int32_t", "float")]
+    assert names == [f[0] for f in binding.GdrProblem._fields_]
 
 
 A = 1 << 20   # fake device addresses, spaced far apart, 16-byte aligned
