@@ -82,3 +82,24 @@ def test_decode_in_kernel_l2norm(gpu_lib, w):
     torch.cuda.synchronize()
     ro, rs = oracle_normalised(inp)
     check(o.cpu().numpy(), s.cpu().numpy(), ro[:, 0], rs, w.dtype, f"decode {w.name}")
+
+
+@pytest.mark.parametrize("idx,heads", [(1, [(0, 2), (0, 9)]), (2, [(1, 4)]), (3, [(1, 17)])],
+                         ids=["gdn_T4096", "kda_B4_T8192", "gqa_B2_T16000"])
+def test_in_kernel_l2norm_full_size(gpu_lib, idx, heads):
+    """Full-size workloads with raw q/k rows normalised in the kernels, in the
+    bench's launch configuration, against sampled scans of the oracle on the
+    same raw rows normalised in fp64."""
+    import dataclasses
+    import torch
+    w = WORKLOADS[idx].with_(normalize_qk=False)
+    inp = make_inputs(w)
+    t = to_device(inp)
+    o, s = gpu_lib.gdr_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["initial_state"],
+                                 scale=inp.scale, qk_l2norm=True)
+    torch.cuda.synchronize()
+    o, s = o.cpu().numpy(), s.cpu().numpy()
+    ninp = dataclasses.replace(inp, q=oracle.l2norm_rows(inp.q), k=oracle.l2norm_rows(inp.k))
+    ref = oracle.recurrence_heads(ninp, heads)
+    for (b, hv), (ro, rs) in ref.items():
+        check(o[b, :, hv], s[b, hv], ro, rs, w.dtype, f"l2norm {w.name} head ({b}, {hv})")

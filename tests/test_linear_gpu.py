@@ -65,20 +65,26 @@ def test_linear_prep_has_no_ut_transform(gpu_lib, w):
     assert torch.equal(ins["m_inv"], eye)
 
 
-def test_linear_full_size_sampled_heads(gpu_lib):
-    """The 4096-token, 12-head workload at full size, in the bench's launch
-    configuration, against sampled heads."""
+FULL = [(1, [(0, 0), (0, 5), (0, 11)]), (2, [(0, 3), (3, 15)]), (3, [(0, 1), (1, 30)]),
+        (4, [(0, 7)])]
+
+
+@pytest.mark.parametrize("idx,heads", FULL, ids=[WORKLOADS[i].name for i, _ in FULL])
+def test_linear_full_size_sampled_heads(gpu_lib, idx, heads):
+    """Every large workload at full size, in the bench's launch configuration
+    (automatic segments and slabs: the linear rule's own scan), against
+    sampled (batch, value head) scans."""
     import torch
-    w = WORKLOADS[1]
+    w = WORKLOADS[idx]
     inp = make_inputs(w)
     t = to_device(inp)
-    o, s = gpu_lib.gdr_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], None,
+    o, s = gpu_lib.gdr_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["initial_state"],
                                  scale=inp.scale, rule="linear")
     torch.cuda.synchronize()
     o, s = o.cpu().numpy(), s.cpu().numpy()
-    ref = oracle.recurrence_heads(inp, [(0, 0), (0, 5), (0, 11)], rule="linear")
+    ref = oracle.recurrence_heads(inp, heads, rule="linear")
     for (b, hv), (ro, rs) in ref.items():
-        check(o[b, :, hv], s[b, hv], ro, rs, w.dtype, f"linear full size head {hv}")
+        check(o[b, :, hv], s[b, hv], ro, rs, w.dtype, f"linear {w.name} head ({b}, {hv})")
 
 
 @pytest.mark.parametrize("w", [WORKLOADS[3].with_(B=2, T=12), WORKLOADS[2].with_(B=1, T=12)],
