@@ -9,7 +9,9 @@
 // (per-channel decay: the prep kernel folds exp(gamma) into the q, k
 // fragments, so the row scales are 1.)  For the decayed linear attention
 // (no erase term) M = I, so W^ = diag(beta exp(gamma_last - gamma)) k and
-// A^ = A_qk, and Z = v: the same loop with the prediction dropped.
+// A^ = A_qk, and Z = v: the same loop with the prediction dropped.  With
+// 64-column slabs that rule has its own instantiation (LIN): Z = v needs
+// no state, so it is staged a step ahead and a step has one barrier.
 //
 // The state update is affine in S: S_{n+1} = A_n S_n + B_n.  A sequence cut
 // into segments is therefore run in two passes:
@@ -33,7 +35,7 @@
 // stall the wave (in-order issue) while the memory pipeline drains them.
 // Only the B operands S and Z cross between waves, through LDS in fragment
 // order (accumulator tiles are B fragments, see gdr_device.hpp), with two
-// barriers per chunk.  The output is formed transposed,
+// barriers per chunk (one for LIN).  The output is formed transposed,
 // o^T = S^T q^T + Z^T A^T: the B fragments of S and Z are also A fragments of
 // S^T and Z^T, and the q and A^ fragments are B fragments of q^T and A^T, so
 // no operand moves, and each lane ends up with four consecutive columns of
@@ -98,7 +100,6 @@ __device__ long long gdr_scan_prof[64 * 16 * 4];
 
 constexpr int kScanFull = 0;
 constexpr int kScanChain = 1;
-constexpr int kScanBV = 64;     // widest slab: state columns per workgroup
 constexpr int kScanWaves = 4;
 
 
