@@ -1,6 +1,10 @@
 """Build libgdr.so (HIP, gfx950) in-tree with hipcc.
 
     python -m chunkwise_gated_delta_cumsum_amd.build
+
+The host logic (gdr_api.hip) and the kernel launchers (one translation unit
+per kernel family) compile in parallel to objects under _build/, which are
+then linked into the shared library.
 """
 from __future__ import annotations
 
@@ -8,13 +12,17 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = [os.path.join(CSRC, "gdr_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in (
+    "gdr_api.hip", "gdr_launch_prep.hip", "gdr_launch_scan_f16.hip", "gdr_launch_scan_lin.hip",
+    "gdr_launch_scan_f32.hip", "gdr_launch_decode.hip")]
+OBJDIR = os.path.join(ROOT, "_build")
 DEPS = SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + [
     os.path.join(INCLUDE, "gdr.h")]
 
@@ -27,7 +35,7 @@ def hipcc() -> str:
 
 
 def flags():
-    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             # packed fp32 VALU ops stay off (see the numerics notes in gdr.h)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # MFMA accumulators in ordinary VGPRs: the state and the products
@@ -36,18 +44,38 @@ def flags():
             "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + ["-o", tmp] + SOURCES
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines()
                     if "packed-fp32-ops" not in l and l.strip())
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out:
-        print(out)
+    return res.returncode, out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(OBJDIR, os.path.basename(src)[:-4] + "." + tag + ".o") for src in SOURCES]
+    cmds = [[hipcc()] + flags() + ["-c", "-o", obj, src] for src, obj in zip(SOURCES, objs)]
+    if verbose:
+        for cmd in cmds:
+            print(" ".join(cmd), flush=True)
+    with ThreadPoolExecutor(max_workers=min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
+        results = list(ex.map(_run, cmds))
+    for cmd, (rc, out) in zip(cmds, results):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) for {cmd[-1]}:\n{out}")
+        if verbose and out:
+            print(out)
+    tmp = LIB + ".tmp" + tag
+    link = [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, out = _run(link)
+    for obj in objs:
+        if os.path.exists(obj):
+            os.remove(obj)
+    if rc != 0:
+        raise RuntimeError(f"hipcc link failed ({rc}):\n{out}")
     os.replace(tmp, LIB)
     return LIB
 

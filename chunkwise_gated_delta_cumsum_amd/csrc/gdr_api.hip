@@ -1,8 +1,9 @@
 // C ABI of the chunkwise gated delta rule forward pass (declared in gdr.h).
 //
 // Host side only: argument validation (no HIP call before it passes), the
-// workspace layout, the gfx950 check, and the launches of the two kernels
-// on the caller's stream.  The library allocates nothing.
+// workspace layout, the gfx950 check, and the launches of the kernels on the
+// caller's stream (the launchers, one translation unit per kernel family,
+// are declared in gdr_launch.hpp).  The library allocates nothing.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -11,25 +12,11 @@
 #include <cstring>
 
 #include "gdr.h"
-#include "gdr_decode.hpp"
-#include "gdr_device.hpp"
-#include "gdr_prep_kda.hpp"
-#include "gdr_scan.hpp"
+#include "gdr_launch.hpp"
 
 using namespace gdr;
 
 namespace {
-
-struct Prob {
-  int B, T, H, HV, K, V, N;
-  bool perch, f32;
-  float scale;
-  size_t es;        // bytes per q/k/v element and per workspace fragment element
-  int nseg, seg_len; // sequence segments of the state scan
-  int bv;            // state columns per scan workgroup (32 or 64)
-  bool l2norm;       // L2-normalise the q and k rows in the prep kernels
-  bool linear;       // decayed linear attention (no erase term)
-};
 
 // Number of sequence segments for the state scan.  One segment runs the
 // serial scan over all N chunks with B*HV*V/64 workgroups.  P segments run a
@@ -171,101 +158,10 @@ gdr_status check_device() {
   return ok ? GDR_OK : GDR_ERR_DEVICE;
 }
 
-template <class Kern, class Args>
-gdr_status launch(Kern kern, unsigned grid, unsigned block, Args& args, hipStream_t s) {
-  void* kargs[] = {&args};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid),
-                                       dim3(block), kargs, 0, s);
-  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
-}
-
-template <int K, bool PERCH, class P>
-gdr_status launch_prep_k(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
-  // (batch, q/k head, chunk) units rounded up to the 8 XCDs, times the
-  // value heads of each q/k head; surplus workgroups exit
-  const size_t units8 = ((size_t)r.B * r.H * r.N + 7) / 8 * 8;
-  const unsigned grid = (unsigned)(units8 * (r.HV / r.H));
-  if constexpr (PERCH) {
-    if (dump) return launch(chunk_prep_kda_kernel<K, P, true>, grid, 256, a, s);
-    return launch(chunk_prep_kda_kernel<K, P, false>, grid, 256, a, s);
-  } else {
-    if (dump) return launch(chunk_prep_kernel<K, P, true>, grid, 256, a, s);
-    return launch(chunk_prep_kernel<K, P, false>, grid, 256, a, s);
-  }
-}
-
-template <bool PERCH, class P>
-gdr_status launch_prep_p(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
-  return r.K == 64 ? launch_prep_k<64, PERCH, P>(r, a, dump, s)
-                   : launch_prep_k<128, PERCH, P>(r, a, dump, s);
-}
-
-gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
-  if (r.f32)
-    return r.perch ? launch_prep_p<true, PolicyF32>(r, a, dump, s)
-                   : launch_prep_p<false, PolicyF32>(r, a, dump, s);
-  return r.perch ? launch_prep_p<true, PolicyF16>(r, a, dump, s)
-                 : launch_prep_p<false, PolicyF16>(r, a, dump, s);
-}
-
-template <int K, int V, bool PERCH, class P, int BV>
-gdr_status launch_scan_kvb(const Prob& r, ScanArgs& a, hipStream_t s) {
-  const size_t BH = (size_t)r.B * r.HV;
-  auto grid_for = [](size_t units, int nslab) {
-    // units rounded up to a multiple of the 8 XCDs; surplus workgroups exit
-    return (unsigned)((units + 7) / 8 * 8 * nslab);
-  };
-  gdr_status st;
-  if (r.nseg > 1) {
-    st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain, BV>,
-                grid_for(BH * (r.nseg - 1), (K + V) / BV), kScanWaves * 64, a, s);
-    if (st != GDR_OK) return st;
-  }
-  return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, BV>,
-                grid_for(BH * r.nseg, V / BV), kScanWaves * 64, a, s);
-}
-
-// The linear rule with 64-column slabs runs its own instantiation (no Y, one
-// barrier per chunk step); with 32-column slabs it takes the general kernels,
-// which drop the prediction term at run time.
-template <int K, int V, bool PERCH, class P>
-gdr_status launch_scan_lin(const Prob& r, ScanArgs& a, hipStream_t s) {
-  const size_t BH = (size_t)r.B * r.HV;
-  auto grid_for = [](size_t units, int nslab) {
-    return (unsigned)((units + 7) / 8 * 8 * nslab);
-  };
-  gdr_status st;
-  if (r.nseg > 1) {
-    st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain, 64, true>,
-                grid_for(BH * (r.nseg - 1), (K + V) / 64), kScanWaves * 64, a, s);
-    if (st != GDR_OK) return st;
-  }
-  return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, 64, true>,
-                grid_for(BH * r.nseg, V / 64), kScanWaves * 64, a, s);
-}
-
-template <int K, int V, bool PERCH, class P>
-gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
-  if (r.linear && r.bv == 64) return launch_scan_lin<K, V, PERCH, P>(r, a, s);
-  return r.bv == 32 ? launch_scan_kvb<K, V, PERCH, P, 32>(r, a, s)
-                    : launch_scan_kvb<K, V, PERCH, P, 64>(r, a, s);
-}
-
-template <bool PERCH, class P>
-gdr_status launch_scan_p(const Prob& r, ScanArgs& a, hipStream_t s) {
-  if (r.K == 64)
-    return r.V == 64 ? launch_scan_kv<64, 64, PERCH, P>(r, a, s)
-                     : launch_scan_kv<64, 128, PERCH, P>(r, a, s);
-  return r.V == 64 ? launch_scan_kv<128, 64, PERCH, P>(r, a, s)
-                   : launch_scan_kv<128, 128, PERCH, P>(r, a, s);
-}
-
 gdr_status launch_scan(const Prob& r, ScanArgs& a, hipStream_t s) {
-  if (r.f32)
-    return r.perch ? launch_scan_p<true, PolicyF32>(r, a, s)
-                   : launch_scan_p<false, PolicyF32>(r, a, s);
-  return r.perch ? launch_scan_p<true, PolicyF16>(r, a, s)
-                 : launch_scan_p<false, PolicyF16>(r, a, s);
+  if (r.f32) return launch_scan_f32(r, a, s);
+  if (r.linear && r.bv == 64) return launch_scan_f16_linear(r, a, s);
+  return launch_scan_f16(r, a, s);
 }
 
 PrepArgs prep_args(const Prob& r, const void* q, const void* k, const float* g,
@@ -311,30 +207,6 @@ gdr_status check_ws(const Prob& r, const void* ws, size_t ws_bytes) {
 int decode_columns(const gdr_problem* p) {
   if (p->scan_slab != 0) return p->scan_slab < p->V ? p->scan_slab : p->V;
   return p->V;   // whole rows: measured best or equal on the decode batches
-}
-
-template <int K, int V, int VB, bool PERCH>
-gdr_status launch_decode_kvb(bool f32, DecodeArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((size_t)a.B * a.HV * (V / VB));
-  if (f32) return launch(decode_step_kernel<K, V, VB, PERCH, float>, grid, 256, a, s);
-  return launch(decode_step_kernel<K, V, VB, PERCH, uint16_t>, grid, 256, a, s);
-}
-
-template <int K, int V, bool PERCH>
-gdr_status launch_decode_kv(int vb, bool f32, DecodeArgs& a, hipStream_t s) {
-  if (vb == 32) return launch_decode_kvb<K, V, 32, PERCH>(f32, a, s);
-  if constexpr (V == 128)
-    if (vb == 128) return launch_decode_kvb<K, V, 128, PERCH>(f32, a, s);
-  return launch_decode_kvb<K, V, 64, PERCH>(f32, a, s);
-}
-
-template <bool PERCH>
-gdr_status launch_decode_p(int K, int V, int vb, bool f32, DecodeArgs& a, hipStream_t s) {
-  if (K == 64)
-    return V == 64 ? launch_decode_kv<64, 64, PERCH>(vb, f32, a, s)
-                   : launch_decode_kv<64, 128, PERCH>(vb, f32, a, s);
-  return V == 64 ? launch_decode_kv<128, 64, PERCH>(vb, f32, a, s)
-                 : launch_decode_kv<128, 128, PERCH>(vb, f32, a, s);
 }
 
 }  // namespace
@@ -386,8 +258,7 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   const bool f32 = p->qkv_dtype == GDR_F32;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int vb = decode_columns(p);
-  return p->g_per_channel ? launch_decode_p<true>(p->K, p->V, vb, f32, a, hs)
-                          : launch_decode_p<false>(p->K, p->V, vb, f32, a, hs);
+  return launch_decode(p->K, p->V, vb, p->g_per_channel == 1, f32, a, hs);
 }
 
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {

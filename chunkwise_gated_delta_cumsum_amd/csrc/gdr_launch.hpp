@@ -1,0 +1,44 @@
+// Kernel launchers of the library, shared by gdr_api.hip (the host logic of
+// the C ABI) and the launcher translation units, one per kernel family
+// (gdr_launch_prep.hip, gdr_launch_scan_f16.hip, gdr_launch_scan_lin.hip,
+// gdr_launch_scan_f32.hip, gdr_launch_decode.hip), which instantiate the
+// kernels and compile in parallel.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "gdr.h"
+#include "gdr_decode.hpp"
+#include "gdr_prep_kda.hpp"
+#include "gdr_scan.hpp"
+
+namespace gdr {
+
+// A validated problem (see validate in gdr_api.hip).
+struct Prob {
+  int B, T, H, HV, K, V, N;
+  bool perch, f32;
+  float scale;
+  size_t es;        // bytes per q/k/v element and per workspace fragment element
+  int nseg, seg_len; // sequence segments of the state scan
+  int bv;            // state columns per scan workgroup (32 or 64)
+  bool l2norm;       // L2-normalise the q and k rows in the prep kernels
+  bool linear;       // decayed linear attention (no erase term)
+};
+
+template <class Kern, class Args>
+inline gdr_status launch(Kern kern, unsigned grid, unsigned block, Args& args, hipStream_t s) {
+  void* kargs[] = {&args};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid),
+                                       dim3(block), kargs, 0, s);
+  return e == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+// Both stages and the decode step, on the caller's stream.
+gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s);
+gdr_status launch_scan_f16(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_scan_f16_linear(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_scan_f32(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_decode(int K, int V, int vb, bool perch, bool f32, DecodeArgs& a,
+                         hipStream_t s);
+
+}  // namespace gdr
