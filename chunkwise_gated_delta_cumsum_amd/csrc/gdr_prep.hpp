@@ -457,7 +457,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
   lds_barrier();
   GDR_PPROF(1);
 
+  // ---- 2. decayed dots (gram_tiles) ----------------------------------------
+  f32x4 aqT[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aqT[j] = zero4();
+  switch (wave) {
+    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
+                                   a.linear != 0, r, grp, aqT); break;
+  }
+
   // ---- q and k for the scan, in its fragment order -------------------------
+  // (after the Gram products, so that their stores drain while the inverse
+  // runs; before the barrier after which M^-T overwrites the q tile)
   // Read straight from the inputs, an MFMA fragment would touch 16 rows per
   // 16 lanes, which the vector memory path serves at a quarter of its
   // contiguous rate; here the rows already sit in LDS, so each query head's
@@ -483,21 +500,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
       __builtin_nontemporal_store(qf, reinterpret_cast<frag_t*>(qd + (size_t)pc * 8));
       __builtin_nontemporal_store(kf, reinterpret_cast<frag_t*>(kd + (size_t)pc * 8));
     }
-  }
-
-  // ---- 2. decayed dots (gram_tiles) ----------------------------------------
-  f32x4 aqT[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) aqT[j] = zero4();
-  switch (wave) {
-    case 0: gram_tiles<0, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
-                                   a.linear != 0, r, grp, aqT); break;
-    case 1: gram_tiles<1, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
-                                   a.linear != 0, r, grp, aqT); break;
-    case 2: gram_tiles<2, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
-                                   a.linear != 0, r, grp, aqT); break;
-    default: gram_tiles<3, K, P>(sK, sQ, sL, sGam, sBeta, sRq, sRk, a.scale,
-                                   a.linear != 0, r, grp, aqT); break;
   }
 
   lds_barrier();   // sL complete
