@@ -255,8 +255,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this library runs the forward pass on one GPU; there is no "
-              "multi-GPU path to measure (heads and batches shard across GPUs with no "
-              "communication; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+              "multi-GPU path to measure (independent heads and batches would shard "
+              "across GPUs with no communication).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -22,7 +22,7 @@ checked step by step:
         o  = (q exp(gamma)) S + A_qk r
         S <- diag(exp(gamma_last)) S + (exp(gamma_last - gamma) k)^T (beta r)
 
-Readings where the listing is loose (each also listed in the design doc):
+Readings where the listing is loose:
   * ``(decay * k_n).T`` transposes the last two axes; ``r * beta_n`` scales
     row j of r by beta_j.
   * T not a multiple of C: pad q, k, v, g, beta with zeros (the scalar-g
