@@ -18,22 +18,32 @@ using namespace gdr;
 
 namespace {
 
-// Number of sequence segments for the state scan.  One segment runs the
-// serial scan over all N chunks with B*HV*V/64 workgroups.  P segments run a
-// chain pass (B*HV*(P-1)*(K+V)/64 workgroups of seg_len chunks, each chunk
-// step about 0.7 of a full-pass step), a serial combine (P-1 steps of about
-// 1.7 full-pass steps each) and the full pass (B*HV*P*V/64 workgroups of
-// seg_len chunks).  A pass with up to 256 workgroups (one per compute unit
-// of an MI355X) takes seg_len steps; beyond that two workgroups share a
-// compute unit at about 1.6x the step time, in rounds of 512.  The constants
+// Cost of the state scan, in 64-column full-pass chunk steps, with P
+// segments of L chunks and BV-column slabs.  One segment runs the serial scan
+// over all N chunks with B*HV*V/BV workgroups.  P segments run a chain pass
+// (B*HV*(P-1)*(K+V)/BV workgroups of L chunks, each chunk step about 0.7 of a
+// full-pass step), a serial combine (P-1 steps of about 1.7 full-pass steps
+// each) and the full pass (B*HV*P*V/BV workgroups of L chunks).  A pass with
+// up to 256 workgroups (one per compute unit of an MI355X) takes L steps;
+// beyond that two workgroups share a compute unit at about 1.6x the step
+// time, in rounds of 512.  A 32-column step costs about 0.7 of a 64-column
+// one (half the products and state, the same operand stream).  The constants
 // are fitted to measured scan times of the 4096-, 8192-, 16000- and
-// 65536-token workloads over forced segment counts.  The estimate uses problem
-// sizes only, so the workspace size query needs no device query.
-int choose_segments(int BH, int N, int K, int V, int& seg_len) {
-  constexpr double kCU = 256.0, kShare = 1.6, kChain = 0.7, kComb = 1.7;
+// 65536-token workloads and of batched variants (12 to 256 scans) over forced
+// segment counts and both widths.  The estimate uses problem sizes only, so
+// the workspace size query needs no device query.
+double scan_cost(int BH, int K, int V, int BV, int P, int L) {
+  constexpr double kCU = 256.0, kShare = 1.6, kChain = 0.7, kComb = 1.7, kStep32 = 0.7;
   auto pass = [&](double wgs, double steps) {
     return wgs <= kCU ? steps : steps * kShare * std::ceil(wgs / (2.0 * kCU));
   };
+  double t = pass((double)BH * P * (V / BV), L);
+  if (P > 1) t += pass((double)BH * (P - 1) * ((K + V) / BV), L) * kChain + (P - 1) * kComb;
+  return BV == 32 ? t * kStep32 : t;
+}
+
+// Segment count for BV-column slabs (and its cost).
+int choose_segments(int BH, int N, int K, int V, int BV, int& seg_len, double& cost) {
   double best = 1e300;
   int bestP = 1;
   seg_len = N;
@@ -41,8 +51,7 @@ int choose_segments(int BH, int N, int K, int V, int& seg_len) {
     const int L = (N + P - 1) / P;
     const int Pe = (N + L - 1) / L;
     if (Pe != P) continue;
-    double t = pass((double)BH * P * (V / 64), L);
-    if (P > 1) t += pass((double)BH * (P - 1) * ((K + V) / 64), L) * kChain + (P - 1) * kComb;
+    const double t = scan_cost(BH, K, V, BV, P, L);
     // more segments also move more bytes (the chain pass reads k, v and W^
     // once more), which the step counts above do not see: a larger P must
     // win by 5%
@@ -52,6 +61,7 @@ int choose_segments(int BH, int N, int K, int V, int& seg_len) {
       seg_len = L;
     }
   }
+  cost = best;
   return bestP;
 }
 
@@ -78,13 +88,36 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.es = r.f32 ? 4 : 2;
   if (p->scan_segments < 0) return GDR_ERR_ARG;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
+  // The automatic width: 64 columns, or 32 where the cost model prices them
+  // at least 15% cheaper.  The model overrates the narrow slabs by about 10%
+  // when few workgroups run: on the 4096-token, 12-head workload it prices
+  // them 11% cheaper (5 segments against 6) and the two measure the same;
+  // on 48 to 64 scans it prices them 18-20% cheaper and they measure 8-18%
+  // faster.  Both widths were measured only with 16-bit operands,
+  // K = V = 128 and the delta rule (the linear rule's 64-column kernel is a
+  // faster instantiation of its own), so elsewhere the choice stays at 64.
+  const bool try32 = p->scan_slab == 0 && !r.f32 && !r.linear && r.K == 128 && r.V == 128;
+  const int BH = r.B * r.HV;
   r.bv = p->scan_slab != 0 ? p->scan_slab : 64;
   if (p->scan_segments == 0) {
-    r.nseg = choose_segments(r.B * r.HV, r.N, r.K, r.V, r.seg_len);
+    double cost = 0.0, cost32 = 0.0;
+    int len32 = 0;
+    r.nseg = choose_segments(BH, r.N, r.K, r.V, r.bv, r.seg_len, cost);
+    if (try32) {
+      const int nseg32 = choose_segments(BH, r.N, r.K, r.V, 32, len32, cost32);
+      if (cost32 < cost * 0.85) {
+        r.bv = 32;
+        r.nseg = nseg32;
+        r.seg_len = len32;
+      }
+    }
   } else {
     const int want = p->scan_segments < r.N ? p->scan_segments : r.N;
     r.seg_len = (r.N + want - 1) / want;
     r.nseg = (r.N + r.seg_len - 1) / r.seg_len;
+    if (try32 && scan_cost(BH, r.K, r.V, 32, r.nseg, r.seg_len) <
+                     scan_cost(BH, r.K, r.V, 64, r.nseg, r.seg_len) * 0.85)
+      r.bv = 32;
   }
   // grid sizes must fit a 32-bit launch dimension
   if ((uint64_t)r.B * r.HV * r.N + 8ull * r.HV > 0x7fffffffull) return GDR_ERR_SHAPE;

@@ -196,6 +196,28 @@ def test_scan_slab_query(lib):
         assert binding.STATUS_NAMES[call_fwd(lib, bad)] == "GDR_ERR_ARG"
 
 
+def test_scan_width_choice(lib):
+    """The automatic slab width and segment count of the cost model: narrow
+    slabs in one segment where 48-64 scans would leave most compute units
+    idle at 64 columns, 64 columns with segments for few long scans, and 64
+    columns whenever the choice was not measured (fp32, the linear rule,
+    head dims of 64)."""
+    def pick(**kw):
+        p = base(**kw)
+        return gdr.scan_slab(p), gdr.scan_segments(p)
+    assert pick(B=2, T=16000, H=16, HV=32, K=128, V=128) == (32, 1)
+    assert pick(B=4, T=8192, H=16, HV=16, K=128, V=128, per_channel=True) == (32, 1)
+    assert pick(B=1, T=4096, H=12, HV=12, K=128, V=128) == (64, 6)
+    assert pick(B=1, T=65536, H=12, HV=12, K=128, V=128) == (64, 10)
+    assert pick(B=8, T=4000, H=16, HV=32, K=128, V=128) == (64, 1)
+    assert pick(B=2, T=16000, H=16, HV=32, K=128, V=128, dtype="fp32")[0] == 64
+    assert pick(B=2, T=16000, H=16, HV=32, K=128, V=128, rule="linear")[0] == 64
+    assert pick(B=2, T=16000, H=16, HV=32, K=64, V=64)[0] == 64
+    # a forced width is kept; forced segments let the width follow the model
+    assert pick(B=2, T=16000, H=16, HV=32, K=128, V=128, slab=64)[0] == 64
+    assert pick(B=2, T=16000, H=16, HV=32, K=128, V=128, segments=1) == (32, 1)
+
+
 def call_decode(lib, prob, q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, s_in=6 * A,
                 s_out=7 * A, o=8 * A):
     ref = None if prob is None else ctypes.byref(prob)
