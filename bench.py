@@ -11,9 +11,10 @@ HBM before the timed region; the step rotates through several copies of the
 inputs and outputs so that no step finds its data in the 256 MB last-level
 cache.  Prints one JSON line.
 
-Workload (default): B=1, T=4096, H=HV=12, K=V=128, chunk 64, scalar decay,
-bf16 q/k/v, fp32 g/beta/o/state: the 4096-token, 12-local-head shape whose
-intra-chunk matrix memory the scalar-g kernel page estimates.
+Workload (default): the largest single-GPU configuration, grouped heads with
+an initial state: B=2, T=16000, H=16 q/k heads, HV=32 value heads,
+K=V=128, chunk 64, scalar decay, bf16 q/k/v, fp32 g/beta/initial state/o/
+final state.  The other workloads run with --workload NAME.
 """
 from __future__ import annotations
 
@@ -24,17 +25,21 @@ import os
 import sys
 import time
 
-WORKLOAD_DEFAULT = "gdn_bf16_T4096_H12_D128"
+WORKLOAD_DEFAULT = "gqa_bf16_B2_T16000_H16_HV32_D128"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
 
 
 def traffic_model(w):
-    """Algorithmic bytes per launch of each kernel and of the whole method.
+    """Bytes per launch of each stage and of the whole method.
 
-    Each tensor a kernel must read or write is counted once (q/k once per q/k
-    head); the workspace is what the prep kernel hands to the scan kernel.
+    compulsory: the method's own inputs and outputs, each counted once (q/k
+    once per q/k head, o in fp32, the states): for the path, for the prep
+    stage (q, k, g, beta) and for the scan stage (q, k, v, o and the states).
+    design: what each stage of this implementation is built to move, i.e.
+    the compulsory bytes plus the workspace the prep kernel hands to the
+    scan kernel (and the per-channel q/k fragments).
     """
     C = w.chunk
     N = -(-w.T // C)
@@ -51,10 +56,11 @@ def traffic_model(w):
     s0 = state if w.s0_std > 0 else 0
     ws = nch * (C * w.K * wes + C * C * wes + (64 + w.K) * 4)
     qkh = 2 * nch * C * w.K * wes if w.per_channel else 0
-    prep = qk + g + beta + ws + qkh
-    scan = (qkh if w.per_channel else qk) + v + ws + s0 + o + state
+    design = dict(chunk_prep=qk + g + beta + ws + qkh,
+                  state_scan=(qkh if w.per_channel else qk) + v + ws + s0 + o + state)
+    stage = dict(chunk_prep=qk + g + beta, state_scan=qk + v + o + s0 + state)
     compulsory = qk + v + g + beta + o + s0 + state
-    return dict(prep=prep, scan=scan, compulsory=compulsory)
+    return dict(design=design, stage=stage, compulsory=compulsory)
 
 
 def algorithmic_flops(w):
@@ -98,33 +104,81 @@ def measured_traffic(w, stage_kernels):
     return total if found else None
 
 
-def cpu_baseline(inp, budget_s, rule="delta"):
+def measured_mfma(w):
+    """MFMA busy fraction per kernel from the stored rocprofv3 counters
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x compute units), or None
+    when there are none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"counters_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    out = {name: v["mfma_busy_frac"] for name, v in rec["kernels"].items()
+           if "mfma_busy_frac" in v}
+    return out or None
+
+
+# the small workloads whose oracle time is also reported on one thread
+SINGLE_THREAD_BASELINE = ("tiny_fp32_T256_H2_D64", "gdn_bf16_T4096_H12_D128")
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def usable_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
+
+
+def cpu_baseline(inp, budget_s, rule="delta", single_thread=False):
+    """The fp64 oracle recurrence on the host cores, over a bounded sample of
+    the workload: all (batch, value head) scans over a token prefix sized to
+    about budget_s / 2 seconds per pass, repeated to about budget_s.  Reports
+    the median pass as tokens/s, with the fastest pass, the thread count and
+    the CPU model; with single_thread, also one thread on a short prefix."""
     import oracle
     w = inp.w
-    threads = min(os.cpu_count() or 1, w.B * w.HV)
-    # one pass over the whole workload if it fits the budget, else a token prefix
-    Ts = w.T
-    probe_T = min(w.T, 256)
-    t0 = time.perf_counter()
-    oracle.recurrence(inp.q[:, :probe_T], inp.k[:, :probe_T], inp.v[:, :probe_T],
-                      inp.g[:, :probe_T], inp.beta[:, :probe_T], inp.scale,
-                      inp.s0, threads=threads, rule=rule)
-    rate = probe_T / max(time.perf_counter() - t0, 1e-9)     # token positions / s
-    if w.T / rate > budget_s:
-        Ts = max(probe_T, int(rate * budget_s))
-    reps, spent, tokens = 0, 0.0, 0
-    while spent < budget_s * 0.5 or reps == 0:
+    threads = min(usable_cores(), w.B * w.HV)
+
+    def run(Ts, nthreads):
         t0 = time.perf_counter()
         oracle.recurrence(inp.q[:, :Ts], inp.k[:, :Ts], inp.v[:, :Ts], inp.g[:, :Ts],
-                          inp.beta[:, :Ts], inp.scale, inp.s0, threads=threads, rule=rule)
-        spent += time.perf_counter() - t0
-        tokens += w.B * Ts
-        reps += 1
-    sample = (f"fp64 {rule}-rule recurrence on all {w.B * w.HV} (batch, value head) scans, "
-              f"{'all' if Ts == w.T else 'first'} {Ts} of {w.T} tokens, x{reps} passes, "
-              f"{spent:.1f} s")
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample}
+                          inp.beta[:, :Ts], inp.scale, inp.s0, threads=nthreads, rule=rule)
+        return time.perf_counter() - t0
+
+    probe_T = min(w.T, 256)
+    rate = probe_T / max(run(probe_T, threads), 1e-9)          # token positions / s
+    Ts = min(w.T, max(probe_T, int(rate * budget_s / 2)))
+    times = []
+    while sum(times) < budget_s * 0.5 or len(times) < 2:
+        times.append(run(Ts, threads))
+    times.sort()
+    med = times[len(times) // 2] if len(times) % 2 else 0.5 * (times[len(times) // 2 - 1] +
+                                                              times[len(times) // 2])
+    rec = {"value": w.B * Ts / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "min_time_value": w.B * Ts / times[0], "cpu_model": cpu_model(),
+           "sample": (f"fp64 {rule}-rule recurrence (C, -O2, OpenMP over scans) on all "
+                      f"{w.B * w.HV} (batch, value head) scans, "
+                      f"{'all' if Ts == w.T else 'first'} {Ts} of {w.T} tokens, "
+                      f"{len(times)} passes, median {med:.2f} s, min {times[0]:.2f} s")}
+    if single_thread:
+        T1 = min(w.T, 256)
+        t1 = sorted(run(T1, 1) for _ in range(3))[1]
+        rec["single_thread"] = {"value": w.B * T1 / t1, "unit": "tokens/s",
+                                "sample": f"first {T1} tokens, median of 3 passes, {t1:.3f} s"}
+    return rec
 
 
 def decode_traffic(w):
@@ -370,10 +424,11 @@ def main():
     # the two stages of the path; the scan stage is up to two kernels (chain
     # pass, then the full pass that also combines the segment transitions)
     # launched by one gdr_chunk_scan call
-    stages = {"chunk_prep": (prep_ms, tm["prep"], ("chunk_prep",)),
-              "state_scan": (scan_ms, tm["scan"], ("chunk_scan_kernel",))}
+    stages = {"chunk_prep": (prep_ms, ("chunk_prep",)),
+              "state_scan": (scan_ms, ("chunk_scan_kernel",))}
     dom = max(stages, key=lambda k_: stages[k_][0])
-    dom_ms, dom_bytes, dom_kernels = stages[dom]
+    dom_ms, dom_kernels = stages[dom]
+    dom_bytes = tm["stage"][dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = measured_traffic(w, dom_kernels)
     nseg = gdr.scan_segments(prob)
@@ -394,13 +449,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "fp32" else "f16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K,
                    "V": w.V, "chunk": w.chunk,
                    "decay": "per-channel" if w.per_channel else "scalar",
                    "inputs": w.dtype, "initial_state": w.s0_std > 0,
-                   "accumulate": "fp32", "rotating_sets": nsets, "rule": args.rule},
+                   "compute": ("fp32 MFMA" if w.dtype == "fp32" else
+                               "fp16 MFMA operands (exact for bf16 inputs), fp32 accumulation")
+                              + ", fp32 state, gamma and o",
+                   "rotating_sets": nsets, "rule": args.rule},
+        # roofline of the dominant stage: the method's compulsory bytes that
+        # stage must move (its inputs read once, its outputs written once)
+        # over its launch duration; the whole path's fraction beside it, and
+        # the fraction on the bytes this implementation is built to move
+        # (compulsory plus the prep-to-scan workspace) under its own name
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
                      "kernels": list(dom_kernels), "algorithmic_bytes": dom_bytes,
@@ -409,11 +472,15 @@ def main():
                      "scan_segments": nseg, "scan_slab": slab,
                      "path_compulsory_bytes": tm["compulsory"],
                      "path_hbm_frac": tm["compulsory"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak},
+                     "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak,
+                     "design_bytes": tm["design"][dom],
+                     "design_bytes_frac": tm["design"][dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "mfma_busy": measured_mfma(w)},
         "fwd_entry_point_matches": same,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule,
+                                           single_thread=w.name in SINGLE_THREAD_BASELINE)
     print(json.dumps(rec), flush=True)
 
 

@@ -1,8 +1,10 @@
 """Thin ctypes binding of libgdr.so (include/gdr.h).
 
-Argument marshalling only: shapes, dtypes and devices are checked, outputs
-and the workspace are allocated with torch on the inputs' device, and the
-C entry point is called on torch's current stream.  Every step of the
+Argument marshalling only: shapes, dtypes and devices of inputs, caller
+outputs and caller workspaces are checked (host tensors are refused before
+the call, since the library takes device pointers), missing outputs and the
+workspace are allocated with torch on the inputs' device, and the C entry
+point is called on torch's current stream.  Every step of the
 computation runs in the HIP kernels; there is no fallback.  If the library
 is missing, load() raises.
 """
@@ -16,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdr.so")
 
 GDR_F32, GDR_BF16 = 0, 1
+DTYPES = {"fp32": GDR_F32, "bf16": GDR_BF16}   # gdr_dtype of q/k/v and of o
 RULES = {"delta": 0, "linear": 1}   # gdr_rule: gated delta rule, decayed linear attention
 GDR_OK = 0
 STATUS_NAMES = {
@@ -34,7 +37,8 @@ class GdrProblem(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("g_per_channel", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qkv_dtype", ctypes.c_int32),
                 ("scan_segments", ctypes.c_int32), ("scan_slab", ctypes.c_int32),
-                ("qk_l2norm", ctypes.c_int32), ("rule", ctypes.c_int32)]
+                ("qk_l2norm", ctypes.c_int32), ("rule", ctypes.c_int32),
+                ("o_dtype", ctypes.c_int32)]
 
 
 class GdrError(RuntimeError):
@@ -92,11 +96,12 @@ def check(status: int) -> None:
 def problem(B: int, T: int, H: int, HV: int, K: int, V: int, *, chunk: int = 64,
             per_channel: bool = False, scale: Optional[float] = None,
             dtype: str = "bf16", segments: int = 0, slab: int = 0,
-            qk_l2norm: bool = False, rule: str = "delta") -> GdrProblem:
+            qk_l2norm: bool = False, rule: str = "delta",
+            o_dtype: str = "fp32") -> GdrProblem:
     return GdrProblem(B, T, H, HV, K, V, chunk, int(bool(per_channel)),
                       float(K ** -0.5 if scale is None else scale),
-                      {"fp32": GDR_F32, "bf16": GDR_BF16}[dtype], int(segments), int(slab),
-                      int(bool(qk_l2norm)), RULES[rule])
+                      DTYPES[dtype], int(segments), int(slab),
+                      int(bool(qk_l2norm)), RULES[rule], DTYPES[o_dtype])
 
 
 def scan_segments(prob: GdrProblem) -> int:
@@ -117,8 +122,13 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _torch_dtype(name: str):
+    import torch
+    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
 def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
-                  qk_l2norm=False, rule="delta") -> GdrProblem:
+                  qk_l2norm=False, rule="delta", o_dtype="fp32") -> GdrProblem:
     import torch
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
@@ -147,7 +157,7 @@ def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
             raise TypeError(f"{name} must be float32")
     return problem(B, T, H, HV, K, V, chunk=chunk, per_channel=per_channel, scale=scale,
                    dtype="fp32" if q.dtype == torch.float32 else "bf16", segments=segments,
-                   slab=slab, qk_l2norm=qk_l2norm, rule=rule)
+                   slab=slab, qk_l2norm=qk_l2norm, rule=rule, o_dtype=o_dtype)
 
 
 def _check_tensors(dev, **ts):
@@ -160,22 +170,62 @@ def _check_tensors(dev, **ts):
             raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(dev, name, t, shape, dtype):
+    """An output the kernels write: exactly `shape` and `dtype`, contiguous, on `dev`."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _check_tensors(dev, **{name: t})
+
+
+def _check_workspace(dev, ws, nbytes):
+    """A caller workspace: uint8, contiguous, on `dev`, at least `nbytes` bytes."""
+    import torch
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8, got {ws.dtype}")
+    _check_tensors(dev, workspace=ws)
+    if _nbytes(ws) < nbytes:
+        raise ValueError(f"workspace holds {_nbytes(ws)} bytes, the problem needs {nbytes}")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _require_gpu(dev):
+    """The library takes device pointers: refuse host tensors before the call."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+
+
 def _stream(dev) -> ctypes.c_void_p:
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _check_state(name, t, B, HV, K, V):
+    import torch
+    if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (B, HV, K, V)):
+        raise ValueError(f"{name} must be float32 [B, HV, K, V] = {(B, HV, K, V)}")
+
+
 def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
                   scale: Optional[float] = None, *, output_final_state: bool = True,
                   workspace=None, out=None, segments: int = 0, slab: int = 0,
-                  qk_l2norm: bool = False, rule: str = "delta"
+                  qk_l2norm: bool = False, rule: str = "delta", o_dtype: str = "fp32"
                   ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunkwise gated delta rule forward on the GPU.
 
     q, k: [B, T, H, K]; v: [B, T, HV, V] (float32 or bfloat16, one dtype);
     g: [B, T, HV] or [B, T, HV, K] float32 log-decay; beta: [B, T, HV] float32;
-    initial_state: [B, HV, K, V] float32 or None.  scale defaults to K**-0.5.
-    Returns (o [B, T, HV, V] float32, final_state [B, HV, K, V] float32 or None).
+    initial_state: [B, HV, K, V] float32 or None.  scale defaults to K**-0.5;
+    chunk is 64 or 128.
+    Returns (o [B, T, HV, V], final_state [B, HV, K, V] float32 or None); o is
+    float32, or bfloat16 with ``o_dtype="bf16"`` (the fp32 result rounded
+    once, to nearest even).
     ``workspace`` (uint8, at least workspace_size bytes) and ``out`` = (o, S)
     may be passed to avoid allocations.  ``segments`` > 0 asks for that many
     sequence segments in the state scan (0: automatic); ``slab`` (32 or 64)
@@ -188,26 +238,31 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule,
+                         o_dtype)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
-    if initial_state is not None and (initial_state.dtype != torch.float32 or
-                                      initial_state.shape != (B, HV, K, V)):
-        raise ValueError("initial_state must be float32 [B, HV, K, V]")
+    _check_state("initial_state", initial_state, B, HV, K, V)
     nbytes = workspace_size(prob)
     if nbytes == 0:
         check(lib.gdr_chunk_fwd(ctypes.byref(prob), *([None] * 8), None, 0, None))
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    odt = _torch_dtype(o_dtype)
+    if workspace is not None:
+        _check_workspace(dev, workspace, nbytes)
     if out is not None:
         o, s = out
-    else:
-        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+        _check_out(dev, "o", o, (B, T, HV, V), odt)
+        _check_out(dev, "final_state", s, (B, HV, K, V), torch.float32)
+    _require_gpu(dev)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if out is None:
+        o = torch.empty((B, T, HV, V), dtype=odt, device=dev)
         s = (torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
              if output_final_state else None)
     st = lib.gdr_chunk_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(initial_state), _ptr(o), _ptr(s), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(dev))
+                           _nbytes(workspace), _stream(dev))
     check(st)
     return o, s
 
@@ -230,8 +285,14 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
     if V is not None:
         prob.V = V
     nbytes = workspace_size(prob)
+    if nbytes == 0:
+        check(lib.gdr_chunk_prep(ctypes.byref(prob), *([None] * 4), None, 0,
+                                 *([None] * 4), None))
+    if workspace is not None:
+        _check_workspace(dev, workspace, nbytes)
+    _require_gpu(dev)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ins: Dict[str, torch.Tensor] = {}
     if inspect:
         B, T, H, K = q.shape
@@ -243,7 +304,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
                    a_qk=torch.empty((B, HV, N, chunk, chunk), dtype=torch.float32, device=dev),
                    m_inv=torch.empty((B, HV, N, chunk, chunk), dtype=torch.float32, device=dev))
     st = lib.gdr_chunk_prep(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(g), _ptr(beta),
-                            _ptr(workspace), workspace.numel(), _ptr(ins.get("gamma")),
+                            _ptr(workspace), _nbytes(workspace), _ptr(ins.get("gamma")),
                             _ptr(ins.get("a_kk")), _ptr(ins.get("a_qk")), _ptr(ins.get("m_inv")),
                             _stream(dev))
     check(st)
@@ -252,7 +313,8 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
 
 def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 64,
                    scale: Optional[float] = None, *, out=None, segments: int = 0,
-                   slab: int = 0, qk_l2norm: bool = False, rule: str = "delta"):
+                   slab: int = 0, qk_l2norm: bool = False, rule: str = "delta",
+                   o_dtype: str = "fp32"):
     """Run the state-scan stage on a workspace filled by gdr_chunk_prep.
 
     ``out`` = (o, final_state) reuses caller tensors (final_state may be None).
@@ -261,29 +323,41 @@ def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int =
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, initial_state=initial_state)
-    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule,
+                         o_dtype)
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
+    _check_state("initial_state", initial_state, B, HV, K, V)
+    nbytes = workspace_size(prob)
+    if nbytes == 0:
+        check(lib.gdr_chunk_scan(ctypes.byref(prob), *([None] * 6), None, 0, None))
+    _check_workspace(dev, workspace, nbytes)
+    odt = _torch_dtype(o_dtype)
     if out is not None:
         o, s = out
-    else:
-        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+        _check_out(dev, "o", o, (B, T, HV, V), odt)
+        _check_out(dev, "final_state", s, (B, HV, K, V), torch.float32)
+    _require_gpu(dev)
+    if out is None:
+        o = torch.empty((B, T, HV, V), dtype=odt, device=dev)
         s = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     st = lib.gdr_chunk_scan(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(initial_state),
-                            _ptr(o), _ptr(s), _ptr(workspace), workspace.numel(), _stream(dev))
+                            _ptr(o), _ptr(s), _ptr(workspace), _nbytes(workspace), _stream(dev))
     check(st)
     return o, s
 
 
 def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None, *,
                     out=None, inplace: bool = False, slab: int = 0, qk_l2norm: bool = False,
-                    rule: str = "delta") -> Tuple["torch.Tensor", "torch.Tensor"]:
+                    rule: str = "delta", o_dtype: str = "fp32"
+                    ) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """One decode step (one token per sequence) on the GPU.
 
     q, k: [B, H, K]; v: [B, HV, V] (float32 or bfloat16, one dtype);
     g: [B, HV] or [B, HV, K] float32 log-decay; beta: [B, HV] float32;
     state: [B, HV, K, V] float32 or None (zero state).  scale defaults to
-    K**-0.5.  Returns (o [B, HV, V] float32, new state [B, HV, K, V] float32).
+    K**-0.5.  Returns (o [B, HV, V] float32 (bfloat16 with o_dtype="bf16"),
+    new state [B, HV, K, V] float32).
     With ``inplace`` the new state overwrites ``state``; ``out`` = (o, S) may
     be passed to avoid allocations.  ``slab`` (32, 64 or 128) sets the state
     columns per workgroup (0: automatic).  ``qk_l2norm`` L2-normalises q and
@@ -314,17 +388,22 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     for name, t in (("g", g), ("beta", beta)):
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
-    if state is not None and (state.dtype != torch.float32 or state.shape != (B, HV, K, V)):
-        raise ValueError("state must be float32 [B, HV, K, V]")
+    _check_state("state", state, B, HV, K, V)
     if inplace and state is None:
         raise ValueError("inplace needs a state")
     prob = problem(B, 1, H, HV, K, V, per_channel=per_channel, scale=scale,
                    dtype="fp32" if q.dtype == torch.float32 else "bf16", slab=slab,
-                   qk_l2norm=qk_l2norm, rule=rule)
+                   qk_l2norm=qk_l2norm, rule=rule, o_dtype=o_dtype)
+    odt = _torch_dtype(o_dtype)
     if out is not None:
         o, s = out
-    else:
-        o = torch.empty((B, HV, V), dtype=torch.float32, device=dev)
+        _check_out(dev, "o", o, (B, HV, V), odt)
+        if s is None:
+            raise ValueError("out must hold a state tensor")
+        _check_out(dev, "state_out", s, (B, HV, K, V), torch.float32)
+    _require_gpu(dev)
+    if out is None:
+        o = torch.empty((B, HV, V), dtype=odt, device=dev)
         s = state if inplace else torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     st = lib.gdr_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                              _ptr(beta), _ptr(state), _ptr(s), _ptr(o), _stream(dev))

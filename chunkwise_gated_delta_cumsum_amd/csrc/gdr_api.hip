@@ -71,6 +71,7 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
       p->HV % p->H != 0)
     return GDR_ERR_SHAPE;
   if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
+  if (p->o_dtype != GDR_F32 && p->o_dtype != GDR_BF16) return GDR_ERR_DTYPE;
   if (p->g_per_channel != 0 && p->g_per_channel != 1) return GDR_ERR_ARG;
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDR_ERR_ARG;
   if (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) return GDR_ERR_ARG;
@@ -86,6 +87,7 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.l2norm = p->qk_l2norm == 1;
   r.linear = p->rule == GDR_RULE_LINEAR;
   r.es = r.f32 ? 4 : 2;
+  r.obf16 = p->o_dtype == GDR_BF16;
   if (p->scan_segments < 0) return GDR_ERR_ARG;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
   // The automatic width: 64 columns, or 32 where the cost model prices them
@@ -152,7 +154,7 @@ struct Spans {
 };
 
 Spans spans(const Prob& r, const void* q, const void* k, const void* v, const float* g,
-            const float* beta, const float* s0, const float* o, const float* sT,
+            const float* beta, const float* s0, const void* o, const float* sT,
             const void* ws, size_t ws_bytes) {
   const size_t tok = (size_t)r.B * r.T;
   Spans s;
@@ -162,7 +164,7 @@ Spans spans(const Prob& r, const void* q, const void* k, const void* v, const fl
   s.g = {g, tok * r.HV * (r.perch ? r.K : 1) * sizeof(float)};
   s.beta = {beta, tok * r.HV * sizeof(float)};
   s.s0 = {s0, (size_t)r.B * r.HV * r.K * r.V * sizeof(float)};
-  s.o = {o, tok * r.HV * r.V * sizeof(float)};
+  s.o = {o, tok * r.HV * r.V * (r.obf16 ? 2 : 4)};
   s.sT = {sT, (size_t)r.B * r.HV * r.K * r.V * sizeof(float)};
   s.ws = {ws, ws_bytes};
   return s;
@@ -214,11 +216,18 @@ PrepArgs prep_args(const Prob& r, const void* q, const void* k, const float* g,
 }
 
 ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
-                   const float* s0, float* o, float* sT, const void* ws) {
+                   const float* s0, void* o, float* sT, const void* ws) {
   const WsLayout L = layout(r);
   char* base = static_cast<char*>(const_cast<void*>(ws));
   ScanArgs a;
   a.q = q; a.k = k; a.v = v; a.s0 = s0; a.o = o; a.sT = sT;
+  a.o_bf16 = r.obf16 ? 1 : 0;
+  // In place (final_state == initial_state) with sequence segments, the
+  // last segment's workgroups write the final state while workgroups of
+  // other segments may not yet have read their columns of the initial
+  // state.  The chain pass, which runs first, then copies the initial state
+  // into the workspace, and the full pass reads the copy.
+  a.s0_copy = (s0 && s0 == sT && r.nseg > 1) ? reinterpret_cast<float*>(base + L.s0c) : nullptr;
   a.wt = base + L.wt; a.ah = base + L.ah; a.rs = reinterpret_cast<const float*>(base + L.rs);
   a.qh = base + L.qh; a.kh = base + L.kh;
   a.B = r.B; a.T = r.T; a.H = r.H; a.HV = r.HV; a.N = r.N;
@@ -248,12 +257,13 @@ extern "C" {
 
 gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const float* state_in,
-                           float* state_out, float* o, void* stream) {
+                           float* state_out, void* o, void* stream) {
   if (!p) return GDR_ERR_NULL;
   if (p->B < 1 || p->T != 1 || p->H < 1 || p->HV < 1 || p->K < 1 || p->V < 1 ||
       p->HV % p->H != 0)
     return GDR_ERR_SHAPE;
   if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
+  if (p->o_dtype != GDR_F32 && p->o_dtype != GDR_BF16) return GDR_ERR_DTYPE;
   if ((p->g_per_channel != 0 && p->g_per_channel != 1) ||
       (p->qk_l2norm != 0 && p->qk_l2norm != 1) ||
       (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) || !std::isfinite(p->scale))
@@ -275,7 +285,7 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   const Span sb = {beta, heads * sizeof(float)};
   const Span si = {state_in, heads * p->K * p->V * sizeof(float)};
   const Span so = {state_out, si.n};
-  const Span sO = {o, heads * p->V * sizeof(float)};
+  const Span sO = {o, heads * p->V * (p->o_dtype == GDR_BF16 ? 2 : 4)};
   if (out_overlaps(sO, {sq, sk, sv, sg, sb, si, so})) return GDR_ERR_ALIAS;
   if (out_overlaps(so, {sq, sk, sv, sg, sb})) return GDR_ERR_ALIAS;
   if (state_in && state_in != state_out && overlap(si, so)) return GDR_ERR_ALIAS;
@@ -284,6 +294,7 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.s_in = state_in; a.s_out = state_out; a.o = o;
+  a.o_bf16 = p->o_dtype == GDR_BF16 ? 1 : 0;
   a.B = p->B; a.H = p->H; a.HV = p->HV;
   a.scale = p->scale;
   a.l2norm = p->qk_l2norm;
@@ -302,7 +313,7 @@ size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
 
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const float* initial_state,
-                         float* o, float* final_state, void* workspace,
+                         void* o, float* final_state, void* workspace,
                          size_t workspace_bytes, void* stream) {
   Prob r;
   gdr_status st = validate(p, &r);
@@ -363,7 +374,7 @@ gdr_status gdr_chunk_prep(const gdr_problem* p, const void* q, const void* k, co
 }
 
 gdr_status gdr_chunk_scan(const gdr_problem* p, const void* q, const void* k, const void* v,
-                          const float* initial_state, float* o, float* final_state,
+                          const float* initial_state, void* o, float* final_state,
                           void* workspace, size_t workspace_bytes, void* stream) {
   Prob r;
   gdr_status st = validate(p, &r);
@@ -414,6 +425,6 @@ int gdr_chunk_scan_slab(const gdr_problem* p) {
   return r.bv;
 }
 
-int gdr_version(void) { return 200; }   // 0.2.0: gdr_problem gained scan_slab, qk_l2norm and rule
+int gdr_version(void) { return 300; }   // 0.3.0: gdr_problem gained o_dtype
 
 }  // extern "C"

@@ -37,7 +37,8 @@ struct DecodeArgs {
   const float* beta;     // [B, HV]
   const float* s_in;     // [B, HV, K, V] or null (zero state)
   float* s_out;          // [B, HV, K, V]; may equal s_in
-  float* o;              // [B, HV, V]
+  void* o;               // [B, HV, V] fp32, or bf16 when o_bf16
+  int o_bf16;
   int B, H, HV;
   float scale;
   int l2norm;            // 1: L2-normalise q and k first
@@ -149,8 +150,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * c4);
   const f32x4 u = a.linear ? vv : vv - A;
   if (wave == 0 && lane < LPR)
-    *reinterpret_cast<f32x4*>(a.o + (size_t)bh * V + v0 + 4 * c4) =
-        a.scale * (Bq + (bt * sqk) * u);
+    store_o4(a.o, (size_t)bh * V + v0 + 4 * c4, a.scale * (Bq + (bt * sqk) * u), a.o_bf16 != 0);
   const f32x4 bu = (bt * srk) * u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {

@@ -98,6 +98,24 @@ __device__ __forceinline__ float sumsq16(u32x4 v) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Four fp32 values rounded to bf16 (nearest even), as the bits of 8 bytes.
+__device__ __forceinline__ u16x4 bf16x4_rne(f32x4 x) {
+  u16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint16_t, (__bf16)x[i]);
+  return r;
+}
+
+// Stores 4 consecutive o values at element offset e of o (fp32, or bf16
+// when bf16 is set), streamed: o is not read again on the device.
+__device__ __forceinline__ void store_o4(void* o, size_t e, f32x4 x, bool bf16) {
+  if (bf16)
+    __builtin_nontemporal_store(bf16x4_rne(x), reinterpret_cast<u16x4*>(
+                                                   static_cast<uint16_t*>(o) + e));
+  else
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(static_cast<float*>(o) + e));
+}
+
 // Index of this wave in its workgroup, as a scalar.  Branches on it are then
 // uniform scalar branches: an MFMA inside one is skipped as a whole instead of
 // running under a partial EXEC mask, which MFMA does not honour.
@@ -356,8 +374,10 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 //   phi, eend : sequence segments (when more than one): transitions
 //        [B*HV][nseg-1][K][K] in the workspace type (A-fragment order) and
 //        zero-start end states [B*HV][nseg-1][K*V] fp32 (tile order).
+//   s0c : with sequence segments, room for a copy of the initial state
+//        [B*HV][K][V] fp32, used when the state is updated in place.
 struct WsLayout {
-  size_t wt, ah, rs, qh, kh, phi, eend, total;
+  size_t wt, ah, rs, qh, kh, phi, eend, s0c, total;
 };
 
 __host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -373,10 +393,11 @@ __host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, i
   L.rs = off; off = ws_align(off + nchunks * 256 * sizeof(float));
   L.qh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
   L.kh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
-  L.phi = L.eend = off;
+  L.phi = L.eend = L.s0c = off;
   if (nseg > 1) {
     L.phi = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * K * elem);
     L.eend = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * V * sizeof(float));
+    L.s0c = off; off = ws_align(off + nheads * (size_t)K * V * sizeof(float));
   }
   L.total = off;
   return L;

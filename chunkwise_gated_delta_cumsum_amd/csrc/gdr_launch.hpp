@@ -23,6 +23,7 @@ struct Prob {
   int bv;            // state columns per scan workgroup (32 or 64)
   bool l2norm;       // L2-normalise the q and k rows in the prep kernels
   bool linear;       // decayed linear attention (no erase term)
+  bool obf16;        // o stored as bf16 (rounded once from fp32)
 };
 
 template <class Kern, class Args>

@@ -64,7 +64,7 @@ struct ScanArgs {
   const void* k;
   const void* v;
   const float* s0;
-  float* o;
+  void* o;           // [B, T, HV, V] fp32, or bf16 when o_bf16
   float* sT;
   const void* wt;
   const void* ah;
@@ -79,6 +79,9 @@ struct ScanArgs {
   void* phi;         // transitions [BH][nseg-1], each K x K in A-fragment order
                      // [K/16 row tiles][K/32 k blocks][64 lanes][8], workspace type
   float* eend;       // zero-start end states, tile order [BH][nseg-1][K*V]
+  int o_bf16;        // 1: o is stored as bf16
+  float* s0_copy;    // chain pass: when set, copy s0 here [BH][K][V] (the full
+                     // pass then reads this copy: the state is updated in place)
 };
 
 #ifdef GDR_SCAN_PROFILE
@@ -445,9 +448,8 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     for (int i = 0; i < ONI; ++i) {
       const int t = n * C + CR * w + ORPI * i + lane / OLPR;
       if (t < T)
-        // streamed: o is not read again on the device by this path
-        __builtin_nontemporal_store(orow_v[i], reinterpret_cast<f32x4*>(
-            a.o + (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % OLPR) * 4));
+        store_o4(a.o, (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % OLPR) * 4,
+                 orow_v[i], a.o_bf16 != 0);
     }
   };
 
@@ -678,6 +680,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   int unit, sv;
   if (!unit_block(a.B * a.HV * nsegu, NSLAB, unit, sv)) return;
   const int wv = wave_id();
+  if constexpr (!FULL) {
+    // in-place state: the first segment's first slab copies the head's
+    // initial state before the full pass (a later launch) overwrites it
+    if (a.s0_copy && a.s0 && unit % nsegu == 0 && sv == 0) {
+      const size_t base = (size_t)(unit / nsegu) * K * V;
+      for (int e = threadIdx.x * 4; e < K * V; e += NW * 64 * 4)
+        *reinterpret_cast<f32x4*>(a.s0_copy + base + e) =
+            *reinterpret_cast<const f32x4*>(a.s0 + base + e);
+    }
+  }
   GDR_WGT(FULL ? 3 : 1, 0);
   auto run = [&](auto phi) {
     constexpr bool PHI = decltype(phi)::value;

@@ -5,6 +5,15 @@
 
 namespace gdr {
 
+// The full pass reads the chain pass's copy of the initial state when there
+// is one (the state is then updated in place, see ScanArgs::s0_copy).
+inline ScanArgs full_pass_args(const ScanArgs& a) {
+  ScanArgs f = a;
+  if (a.s0_copy) f.s0 = a.s0_copy;
+  f.s0_copy = nullptr;
+  return f;
+}
+
 template <int K, int V, bool PERCH, class P, int BV>
 gdr_status launch_scan_kvb(const Prob& r, ScanArgs& a, hipStream_t s) {
   const size_t BH = (size_t)r.B * r.HV;
@@ -18,8 +27,9 @@ gdr_status launch_scan_kvb(const Prob& r, ScanArgs& a, hipStream_t s) {
                 grid_for(BH * (r.nseg - 1), (K + V) / BV), kScanWaves * 64, a, s);
     if (st != GDR_OK) return st;
   }
+  ScanArgs f = full_pass_args(a);
   return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, BV>,
-                grid_for(BH * r.nseg, V / BV), kScanWaves * 64, a, s);
+                grid_for(BH * r.nseg, V / BV), kScanWaves * 64, f, s);
 }
 
 // The linear rule with 64-column slabs runs its own instantiation (no Y, one
@@ -37,8 +47,9 @@ gdr_status launch_scan_lin(const Prob& r, ScanArgs& a, hipStream_t s) {
                 grid_for(BH * (r.nseg - 1), (K + V) / 64), kScanWaves * 64, a, s);
     if (st != GDR_OK) return st;
   }
+  ScanArgs f = full_pass_args(a);
   return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, 64, true>,
-                grid_for(BH * r.nseg, V / 64), kScanWaves * 64, a, s);
+                grid_for(BH * r.nseg, V / 64), kScanWaves * 64, f, s);
 }
 
 // LINEAR selects the linear rule's instantiation (64-column slabs);

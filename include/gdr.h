@@ -23,7 +23,7 @@
  *                  [B, T, HV, K] fp32 when g_per_channel = 1 (KDA form)
  *   beta           [B, T, HV]      fp32
  *   initial_state  [B, HV, K, V]   fp32, or NULL for a zero state
- *   o              [B, T, HV, V]   fp32 (output)
+ *   o              [B, T, HV, V]   o_dtype: fp32, or bf16 (output)
  *   final_state    [B, HV, K, V]   fp32 (output), or NULL to skip
  *
  * Ownership: the caller allocates and owns every buffer, the workspace
@@ -42,7 +42,7 @@
  *
  * Numerics: with GDR_BF16 inputs the matrix products run on MFMA with fp16
  * operands and fp32 accumulation; the state, gamma, exponentials and o are
- * fp32.  bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
+ * fp32 (o is rounded to bf16 only as it is stored, when o_dtype asks).  bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
  * inputs every product runs in fp32.  With per-channel decay the decay is
  * folded into fp16 operands, which grow as exp(sum of the positive g of a
  * channel within one chunk): that sum must stay below about 8 (g <= 0, the
@@ -62,7 +62,7 @@ typedef enum gdr_status {
   GDR_OK = 0,
   GDR_ERR_NULL = 1,        /* a required pointer (problem, q, k, v, g, beta, o) is NULL */
   GDR_ERR_SHAPE = 2,       /* B, T, H, HV, K or V < 1, or HV % H != 0 */
-  GDR_ERR_DTYPE = 3,       /* qkv_dtype is not a gdr_dtype value */
+  GDR_ERR_DTYPE = 3,       /* qkv_dtype or o_dtype is not a gdr_dtype value */
   GDR_ERR_UNSUPPORTED = 4, /* valid but not built: chunk != 64, K or V not 64 or 128 */
   GDR_ERR_ALIGN = 5,       /* a tensor or workspace pointer is not 16-byte aligned */
   GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query */
@@ -110,6 +110,14 @@ typedef struct gdr_problem {
                                 they enter a product.  0: q and k are used as
                                 given */
   int32_t rule;              /* gdr_rule: GDR_RULE_DELTA (0) or GDR_RULE_LINEAR */
+  int32_t o_dtype;           /* gdr_dtype of o: GDR_F32 (0, the default) or
+                                GDR_BF16, the fp32 result rounded once to
+                                nearest even as it is stored (the scalar-g
+                                kernel page casts its output back to the
+                                input dtype).  Rounding o alone to bf16
+                                costs about 2e-2 relative to max|o| / rms(o)
+                                on the workloads, so fp32 is the form whose
+                                accuracy the library states. */
 } gdr_problem;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when
@@ -127,7 +135,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p,
                          const void* q, const void* k, const void* v,
                          const float* g, const float* beta,
                          const float* initial_state,
-                         float* o, float* final_state,
+                         void* o, float* final_state,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
@@ -161,7 +169,7 @@ gdr_status gdr_chunk_prep(const gdr_problem* p,
 gdr_status gdr_chunk_scan(const gdr_problem* p,
                           const void* q, const void* k, const void* v,
                           const float* initial_state,
-                          float* o, float* final_state,
+                          void* o, float* final_state,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
@@ -184,13 +192,13 @@ gdr_status gdr_chunk_scan(const gdr_problem* p,
  *   state_in  [B, HV, K, V] fp32, or NULL for a zero state
  *   state_out [B, HV, K, V] fp32 (required); state_out == state_in updates
  *             the state in place (a partial overlap is GDR_ERR_ALIAS)
- *   o     [B, HV, V] fp32
+ *   o     [B, HV, V] o_dtype (fp32 or bf16)
  * No workspace.  Validation, errors and streams as for gdr_chunk_fwd.  The
  * kernel reads and writes the state once: it is bound by HBM bandwidth. */
 gdr_status gdr_decode_step(const gdr_problem* p,
                            const void* q, const void* k, const void* v,
                            const float* g, const float* beta,
-                           const float* state_in, float* state_out, float* o,
+                           const float* state_in, float* state_out, void* o,
                            void* stream);
 
 /* Number of sequence segments the state scan of problem `p` uses (1: one

@@ -17,14 +17,28 @@ arithmetic.
 * ``l2norm_rows`` -- fp64 row normaliser x * rsqrt(sum x^2 + 1e-6), the
                      reference for in-kernel q/k normalisation.
 
-Pins (tests/test_oracle_*.py, CPU only): chunk form == recurrence for several
-chunk sizes, closed forms (beta = 0 and g = 0; orthonormal keys; repeated
-unit key; reset by g = -800; standard-basis keys with per-channel decay),
-a Kronecker-product brute force on tiny shapes, segment splitting, joint
-linearity, grouped-head equivalence, hand-derived golden values, and the
-three UT inverse forms against each other, and the row normaliser against a
-hand-derived row, its closed-form norm and the zero row.  No function here
-is left unpinned.
+Pins (tests/test_oracle_pins.py, CPU only), one or more per function:
+
+* ``recurrence``       -- hand-derived golden values (tests/golden/), closed
+                          forms (beta = 0 and g = 0; orthonormal keys;
+                          repeated unit key; reset by g = -800;
+                          standard-basis keys with per-channel decay), a
+                          Kronecker-product brute force on tiny shapes,
+                          segment splitting, joint linearity, grouped-head
+                          equivalence with explicit repeat_interleave, and
+                          (linear rule) the page's masked quadratic form.
+* ``recurrence_heads`` -- every (b, hv) scan, and a cut T, equal the
+                          recurrence run on all heads at once bit for bit;
+                          the modulo grouping must differ.
+* ``chunk_forward``    -- equals the recurrence for chunk sizes 1, 16, 64,
+                          128 and T, with scalar and per-channel decay,
+                          grouped heads, an initial state and ragged T.
+* ``decayed_dot``      -- a triple loop over its definition, and the
+                          factored (x k^T) * exp(gamma_i - gamma_j) form.
+* ``ut_inverse_*``     -- the triangular solve, the Neumann series and the
+                          row iteration agree (three forms the pages give).
+* ``l2norm_rows``      -- a hand-derived row, the closed-form norm of any
+                          output row, the kept direction and the zero row.
 """
 from .recurrence import build, num_threads, recurrence, recurrence_heads  # noqa: F401
 from .chunk_form import (chunk_forward, decayed_dot, ut_inverse_neumann,  # noqa: F401

@@ -272,3 +272,81 @@ def test_rule_validation(lib):
     assert binding.STATUS_NAMES[call_decode(lib, bad1)] == "GDR_ERR_ARG"
     lin = base(T=100, rule="linear")
     assert lin.rule == 1 and gdr.workspace_size(lin) == gdr.workspace_size(base(T=100))
+
+
+def test_o_dtype_validation(lib):
+    """o_dtype must be a gdr_dtype; a bf16 o spans half the bytes of an fp32 one."""
+    name = lambda st: binding.STATUS_NAMES[st]
+    bad = base(T=100)
+    bad.o_dtype = 2
+    assert name(call_fwd(lib, bad)) == "GDR_ERR_DTYPE"
+    assert gdr.workspace_size(bad) == 0
+    bad1 = base(T=1)
+    bad1.o_dtype = -1
+    assert name(call_decode(lib, bad1)) == "GDR_ERR_DTYPE"
+    # o placed just below v: B*T*HV*V = 51200 elements, 204800 bytes in fp32
+    # (overlaps v) and 102400 in bf16 (does not)
+    p32, p16 = base(T=100), base(T=100, o_dtype="bf16")
+    o_at = 3 * A - 150000
+    assert name(call_fwd(lib, p32, o=o_at)) == "GDR_ERR_ALIAS"
+    assert name(call_fwd(lib, p16, o=o_at)) != "GDR_ERR_ALIAS"
+    assert gdr.workspace_size(p16) == gdr.workspace_size(p32)
+
+
+def _cpu_inputs(B=1, T=40, H=2, HV=4, K=64, V=64):
+    import torch
+    q = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    return dict(q=q, k=q.clone(), v=torch.zeros(B, T, HV, V, dtype=torch.bfloat16),
+                g=torch.zeros(B, T, HV), beta=torch.zeros(B, T, HV))
+
+
+def test_binding_checks_outputs_and_workspace(lib):
+    """The binding refuses caller outputs and workspaces of the wrong dtype,
+    shape or layout, and host tensors, before the library is called."""
+    import torch
+    t = _cpu_inputs()
+    args = (t["q"], t["k"], t["v"], t["g"], t["beta"])
+    o = torch.empty(1, 40, 4, 64)
+    s = torch.empty(1, 4, 64, 64)
+    with pytest.raises(TypeError, match="o must be"):
+        gdr.gdr_chunk_fwd(*args, out=(o.to(torch.bfloat16), s))
+    with pytest.raises(TypeError, match="o must be"):
+        gdr.gdr_chunk_fwd(*args, out=(o, s), o_dtype="bf16")
+    with pytest.raises(ValueError, match="o must have shape"):
+        gdr.gdr_chunk_fwd(*args, out=(torch.empty(1, 39, 4, 64), s))
+    with pytest.raises(ValueError, match="final_state must have shape"):
+        gdr.gdr_chunk_fwd(*args, out=(o, torch.empty(1, 4, 64, 32)))
+    with pytest.raises(TypeError, match="final_state must be"):
+        gdr.gdr_chunk_fwd(*args, out=(o, s.double()))
+    with pytest.raises(ValueError, match="contiguous"):
+        gdr.gdr_chunk_fwd(*args, out=(torch.empty(1, 40, 64, 4).transpose(2, 3), s))
+    need = gdr.workspace_size(gdr.problem(1, 40, 2, 4, 64, 64))
+    with pytest.raises(TypeError, match="workspace must be uint8"):
+        gdr.gdr_chunk_fwd(*args, workspace=torch.empty(need, dtype=torch.float32))
+    with pytest.raises(ValueError, match="workspace holds"):
+        gdr.gdr_chunk_fwd(*args, workspace=torch.empty(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="initial_state must be"):
+        gdr.gdr_chunk_fwd(*args, torch.empty(1, 4, 64, 63))
+    # a well-formed call on host tensors is refused: the library takes device pointers
+    with pytest.raises(ValueError, match="on a GPU"):
+        gdr.gdr_chunk_fwd(*args, out=(o, s), workspace=torch.empty(need, dtype=torch.uint8))
+    # the stage entry points and decode check the same way
+    with pytest.raises(ValueError, match="workspace holds"):
+        gdr.gdr_chunk_prep(t["q"], t["k"], t["g"], t["beta"], V=64,
+                           workspace=torch.empty(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="workspace holds"):
+        gdr.gdr_chunk_scan(*args, torch.empty(need - 16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="o must have shape"):
+        gdr.gdr_chunk_scan(*args, torch.empty(need, dtype=torch.uint8),
+                           out=(torch.empty(1, 40, 4, 32), s))
+    with pytest.raises(ValueError, match="on a GPU"):
+        gdr.gdr_chunk_scan(*args, torch.empty(need, dtype=torch.uint8), out=(o, s))
+    d = {k_: v_[:, 0].contiguous() for k_, v_ in t.items()}
+    dargs = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    st = torch.zeros(1, 4, 64, 64)
+    with pytest.raises(ValueError, match="o must have shape"):
+        gdr.gdr_decode_step(*dargs, st, out=(torch.empty(1, 4, 32), st))
+    with pytest.raises(TypeError, match="state_out must be"):
+        gdr.gdr_decode_step(*dargs, st, out=(torch.empty(1, 4, 64), st.double()))
+    with pytest.raises(ValueError, match="on a GPU"):
+        gdr.gdr_decode_step(*dargs, st, out=(torch.empty(1, 4, 64), st))

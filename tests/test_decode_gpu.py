@@ -42,6 +42,8 @@ CASES = [
     WORKLOADS[3].with_(B=2, T=1, K=64, V=128, s0_std=0.1),
     WORKLOADS[3].with_(B=2, T=1, K=128, V=64, s0_std=0.1, dtype="fp32"),
     WORKLOADS[2].with_(B=2, T=1, K=64, V=64, s0_std=0.1, dtype="fp32"),
+    WORKLOADS[2].with_(B=2, T=1, H=4, HV=16, s0_std=0.1),              # per-channel, G = 4
+    WORKLOADS[2].with_(B=2, T=1, H=2, HV=4, s0_std=0.1, dtype="fp32"),  # per-channel, G = 2
 ]
 
 

@@ -55,7 +55,7 @@ def test_golden_hand_derived(path):
 
 # ------------------------------------------- chunk form == recurrence -------
 @pytest.mark.parametrize("per_channel", [False, True])
-@pytest.mark.parametrize("C", [1, 16, 64, 200])
+@pytest.mark.parametrize("C", [1, 16, 64, 128, 200])
 @pytest.mark.parametrize("T,H,HV,s0", [(200, 2, 2, False), (130, 1, 2, True),
                                        (77, 2, 4, True)])
 def test_chunk_form_equals_recurrence(per_channel, C, T, H, HV, s0):
@@ -417,3 +417,35 @@ def test_linear_rule_page_form_and_delta_difference():
     o2, s2 = oracle.recurrence(q[:, :1], k[:, :1], v[:, :1], g[:, :1], one[:, :1], 1.0, None)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(s1, s2)
+
+
+# ------------------------------------------------- per-head recurrence ------
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_recurrence_heads_equals_full_recurrence(per_channel):
+    """recurrence_heads (the reference of the full-size sampled-head GPU tests)
+    slices one (b, hv) scan at a time, with q/k head h = hv // G (the
+    repeat_interleave grouping of the sec-03 rearrange step) and the initial
+    state of that head.  Every head, and a cut T, must equal the recurrence
+    run on all heads at once bit for bit (each scan is independent)."""
+    from chunkwise_gated_delta_cumsum_amd.inputs import Workload, make_inputs
+    w = Workload("pin_heads", B=2, T=70, H=2, HV=4, K=8, V=8, per_channel=per_channel,
+                 dtype="fp32", g_mu=1.0, s0_std=0.1, seed=5)
+    inp = make_inputs(w)
+    heads = [(b, hv) for b in range(w.B) for hv in range(w.HV)]
+    for T in (w.T, 33):
+        o, s = oracle.recurrence(inp.q[:, :T], inp.k[:, :T], inp.v[:, :T], inp.g[:, :T],
+                                 inp.beta[:, :T], inp.scale, inp.s0)
+        got = oracle.recurrence_heads(inp, heads, T=T)
+        assert sorted(got) == heads
+        for b, hv in heads:
+            go, gs = got[(b, hv)]
+            assert go.shape == (T, w.V) and gs.shape == (w.K, w.V)
+            np.testing.assert_array_equal(go, o[b, :, hv])
+            np.testing.assert_array_equal(gs, s[b, hv])
+    # the modulo grouping (h = hv % H) is a different map: value head 1 of
+    # batch 0 would read q/k head 1 instead of 0, and must disagree
+    o, _ = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.s0)
+    wrong = oracle.recurrence(inp.q[:1, :, 1:2], inp.k[:1, :, 1:2], inp.v[:1, :, 1:2],
+                              inp.g[:1, :, 1:2], inp.beta[:1, :, 1:2], inp.scale,
+                              inp.s0[:1, 1:2])[0]
+    assert rel(wrong[0, :, 0], o[0, :, 1]) > 1e-3
