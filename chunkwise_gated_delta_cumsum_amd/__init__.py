@@ -5,8 +5,9 @@ declared in include/gdr.h (libgdr.so, built in-tree by ``build.py``); this
 package is the thin Python binding over it plus the seeded input generator.
 """
 from .binding import (GDR_BF16, GDR_F32, EXPORTED, GdrError, GdrProblem, LIB_PATH,  # noqa: F401
-                      check, gdr_chunk_fwd, gdr_chunk_prep, gdr_chunk_scan, gdr_decode_step, load,
+                      NOALLOC_SCRATCH_BYTES, check, gdr_chunk_fwd, gdr_chunk_fwd_noalloc,
+                      gdr_chunk_prep, gdr_chunk_scan, gdr_decode_step, load,
                       problem,
                       scan_segments, scan_slab, status_string, workspace_size)
 
-__version__ = "0.2.0"
+__version__ = "0.3.0"

@@ -25,8 +25,11 @@ STATUS_NAMES = {
     0: "GDR_OK", 1: "GDR_ERR_NULL", 2: "GDR_ERR_SHAPE", 3: "GDR_ERR_DTYPE",
     4: "GDR_ERR_UNSUPPORTED", 5: "GDR_ERR_ALIGN", 6: "GDR_ERR_WORKSPACE",
     7: "GDR_ERR_DEVICE", 8: "GDR_ERR_HIP", 9: "GDR_ERR_ARG", 10: "GDR_ERR_ALIAS",
+    11: "GDR_ERR_SCRATCH",
 }
-EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_prep",
+NOALLOC_SCRATCH_BYTES = 64 << 20    # GDR_NOALLOC_SCRATCH_BYTES in gdr.h
+EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc",
+            "gdr_chunk_prep",
             "gdr_chunk_scan", "gdr_chunk_scan_segments", "gdr_chunk_scan_slab",
             "gdr_decode_step", "gdr_status_string", "gdr_version")
 
@@ -66,6 +69,8 @@ def load():
     lib.gdr_chunk_fwd_workspace_size.restype = sz
     lib.gdr_chunk_fwd.argtypes = [P] + [vp] * 8 + [vp, sz, vp]
     lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_noalloc.argtypes = [P] + [vp] * 8 + [vp]
+    lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunk_prep.argtypes = [P] + [vp] * 4 + [vp, sz] + [vp] * 4 + [vp]
     lib.gdr_chunk_prep.restype = ctypes.c_int
     lib.gdr_chunk_scan.argtypes = [P] + [vp] * 6 + [vp, sz, vp]
@@ -263,6 +268,47 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     st = lib.gdr_chunk_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(initial_state), _ptr(o), _ptr(s), _ptr(workspace),
                            _nbytes(workspace), _stream(dev))
+    check(st)
+    return o, s
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, chunk: int = 64,
+                          scale: Optional[float] = None, *, output_final_state: bool = True,
+                          out=None, segments: int = 0, slab: int = 0,
+                          qk_l2norm: bool = False, rule: str = "delta", o_dtype: str = "fp32"
+                          ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """gdr_chunk_fwd on the library's own device scratch array instead of a
+    workspace (the C entry point allocates nothing; with ``out`` given this
+    wrapper allocates nothing either).  Problems whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES raise GDR_ERR_SCRATCH.  Calls that overlap in time
+    on one GPU share the array and race."""
+    import torch
+    lib = load()
+    dev = q.device
+    _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state)
+    prob = _problem_from(q, k, v, g, beta, chunk, scale, segments, slab, qk_l2norm, rule,
+                         o_dtype)
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    _check_state("initial_state", initial_state, B, HV, K, V)
+    nbytes = workspace_size(prob)
+    if nbytes == 0:     # an invalid problem: the library names the reason
+        check(lib.gdr_chunk_fwd_noalloc(ctypes.byref(prob), *([None] * 8), None))
+    if nbytes > NOALLOC_SCRATCH_BYTES:
+        check(11)       # GDR_ERR_SCRATCH, as the library would return
+    odt = _torch_dtype(o_dtype)
+    if out is not None:
+        o, s = out
+        _check_out(dev, "o", o, (B, T, HV, V), odt)
+        _check_out(dev, "final_state", s, (B, HV, K, V), torch.float32)
+    _require_gpu(dev)
+    if out is None:
+        o = torch.empty((B, T, HV, V), dtype=odt, device=dev)
+        s = (torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
+             if output_final_state else None)
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(s),
+                                   _stream(dev))
     check(st)
     return o, s
 

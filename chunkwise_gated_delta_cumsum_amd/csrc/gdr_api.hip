@@ -10,9 +10,17 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "gdr.h"
 #include "gdr_launch.hpp"
+
+// The workspace of gdr_chunk_fwd_noalloc: one array per device, loaded with
+// the library's code object.  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress (scratch_address below) and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
 
 using namespace gdr;
 
@@ -245,6 +253,64 @@ gdr_status check_ws(const Prob& r, const void* ws, size_t ws_bytes) {
   return GDR_OK;
 }
 
+// Device address of this device's `scratch` array, looked up on the
+// device's first call (with that device current) and kept per device.
+gdr_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_HIP;
+  if (dev < 0 || dev >= 64) return GDR_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return GDR_ERR_HIP;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return GDR_OK;
+}
+
+// Checks shared by gdr_chunk_fwd and gdr_chunk_fwd_noalloc after validation:
+// the required pointers and their alignment, then (once the workspace is
+// known) overlaps between buffers.  ws may be NULL: the library's own
+// scratch array overlaps none of the caller's buffers.
+gdr_status check_fwd_pointers(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* initial_state, const void* o,
+                              const float* final_state) {
+  if (!q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
+                          (const void*)beta, (const void*)initial_state, (const void*)o,
+                          (const void*)final_state})
+    if (ptr && !aligned16(ptr)) return GDR_ERR_ALIGN;
+  return GDR_OK;
+}
+
+gdr_status check_fwd_overlaps(const Prob& r, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* initial_state,
+                              const void* o, const float* final_state, const void* ws,
+                              size_t ws_bytes) {
+  const Spans s = spans(r, q, k, v, g, beta, initial_state, o, final_state, ws, ws_bytes);
+  if (out_overlaps(s.o, {s.q, s.k, s.v, s.g, s.beta, s.s0, s.sT, s.ws})) return GDR_ERR_ALIAS;
+  if (out_overlaps(s.ws, {s.q, s.k, s.v, s.g, s.beta, s.s0, s.sT})) return GDR_ERR_ALIAS;
+  if (out_overlaps(s.sT, {s.q, s.k, s.v, s.g, s.beta})) return GDR_ERR_ALIAS;
+  if (initial_state && final_state && initial_state != final_state && overlap(s.sT, s.s0))
+    return GDR_ERR_ALIAS;
+  return GDR_OK;
+}
+
+// The launches of the whole forward pass on a checked problem.
+gdr_status launch_fwd(const Prob& r, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* initial_state, void* o,
+                      float* final_state, void* ws, hipStream_t hs) {
+  PrepArgs pa = prep_args(r, q, k, g, beta, ws);
+  gdr_status st = launch_prep(r, pa, false, hs);
+  if (st != GDR_OK) return st;
+  ScanArgs sa = scan_args(r, q, k, v, initial_state, o, final_state, ws);
+  return launch_scan(r, sa, hs);
+}
+
 // State columns per decode workgroup: 0 chooses (see decode_columns).
 int decode_columns(const gdr_problem* p) {
   if (p->scan_slab != 0) return p->scan_slab < p->V ? p->scan_slab : p->V;
@@ -318,26 +384,35 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   Prob r;
   gdr_status st = validate(p, &r);
   if (st != GDR_OK) return st;
-  if (!q || !k || !v || !g || !beta || !o) return GDR_ERR_NULL;
-  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
-                          (const void*)beta, (const void*)initial_state, (const void*)o,
-                          (const void*)final_state})
-    if (ptr && !aligned16(ptr)) return GDR_ERR_ALIGN;
+  if ((st = check_fwd_pointers(q, k, v, g, beta, initial_state, o, final_state)) != GDR_OK)
+    return st;
   if ((st = check_ws(r, workspace, workspace_bytes)) != GDR_OK) return st;
-  const Spans s = spans(r, q, k, v, g, beta, initial_state, o, final_state, workspace,
-                        workspace_bytes);
-  if (out_overlaps(s.o, {s.q, s.k, s.v, s.g, s.beta, s.s0, s.sT, s.ws})) return GDR_ERR_ALIAS;
-  if (out_overlaps(s.ws, {s.q, s.k, s.v, s.g, s.beta, s.s0, s.sT})) return GDR_ERR_ALIAS;
-  if (out_overlaps(s.sT, {s.q, s.k, s.v, s.g, s.beta})) return GDR_ERR_ALIAS;
-  if (initial_state && final_state && initial_state != final_state && overlap(s.sT, s.s0))
-    return GDR_ERR_ALIAS;
+  if ((st = check_fwd_overlaps(r, q, k, v, g, beta, initial_state, o, final_state, workspace,
+                               workspace_bytes)) != GDR_OK)
+    return st;
   if ((st = check_device()) != GDR_OK) return st;
+  return launch_fwd(r, q, k, v, g, beta, initial_state, o, final_state, workspace,
+                    static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  PrepArgs pa = prep_args(r, q, k, g, beta, workspace);
-  if ((st = launch_prep(r, pa, false, hs)) != GDR_OK) return st;
-  ScanArgs sa = scan_args(r, q, k, v, initial_state, o, final_state, workspace);
-  return launch_scan(r, sa, hs);
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta,
+                                 const float* initial_state, void* o, float* final_state,
+                                 void* stream) {
+  Prob r;
+  gdr_status st = validate(p, &r);
+  if (st != GDR_OK) return st;
+  if ((st = check_fwd_pointers(q, k, v, g, beta, initial_state, o, final_state)) != GDR_OK)
+    return st;
+  if (layout(r).total > GDR_NOALLOC_SCRATCH_BYTES) return GDR_ERR_SCRATCH;
+  if ((st = check_fwd_overlaps(r, q, k, v, g, beta, initial_state, o, final_state, nullptr,
+                               0)) != GDR_OK)
+    return st;
+  if ((st = check_device()) != GDR_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != GDR_OK) return st;
+  return launch_fwd(r, q, k, v, g, beta, initial_state, o, final_state, ws,
+                    static_cast<hipStream_t>(stream));
 }
 
 gdr_status gdr_chunk_prep(const gdr_problem* p, const void* q, const void* k, const float* g,
@@ -409,6 +484,7 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_HIP: return "GDR_ERR_HIP: a HIP query or kernel launch failed";
     case GDR_ERR_ARG: return "GDR_ERR_ARG: scale must be finite, g_per_channel and qk_l2norm 0 or 1, rule a gdr_rule, scan_segments >= 0, scan_slab 0, 32 or 64 (128 for decode)";
     case GDR_ERR_ALIAS: return "GDR_ERR_ALIAS: an output overlaps an input or another output";
+    case GDR_ERR_SCRATCH: return "GDR_ERR_SCRATCH: the problem needs more workspace than gdr_chunk_fwd_noalloc's GDR_NOALLOC_SCRATCH_BYTES";
     default: return "GDR_ERR_UNKNOWN: unknown status value";
   }
 }

@@ -72,9 +72,16 @@ typedef enum gdr_status {
                               rule not a gdr_rule,
                               scan_segments < 0, or scan_slab not 0, 32 or 64
                               (gdr_decode_step also takes 128) */
-  GDR_ERR_ALIAS = 10       /* an output overlaps an input or the other output
+  GDR_ERR_ALIAS = 10,      /* an output overlaps an input or the other output
                               (final_state == initial_state exactly is allowed) */
+  GDR_ERR_SCRATCH = 11     /* gdr_chunk_fwd_noalloc: the problem needs more
+                              workspace than GDR_NOALLOC_SCRATCH_BYTES */
 } gdr_status;
+
+/* Bytes of the library's own device scratch array behind
+ * gdr_chunk_fwd_noalloc: one array per GPU the library runs on, held until
+ * the process ends. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 
@@ -138,6 +145,28 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p,
                          void* o, float* final_state,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* gdr_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is the library's own
+ * file-scope device array of GDR_NOALLOC_SCRATCH_BYTES (64 MiB) on the
+ * current device; a problem whose gdr_chunk_fwd_workspace_size exceeds it
+ * returns GDR_ERR_SCRATCH before anything is launched (the 4096-token,
+ * 12-head, K = V = 128 problem needs about 49 MiB).  The caller still owns q,
+ * k, v, g, beta, the states and o, with the layouts, validation, errors and
+ * stream semantics of gdr_chunk_fwd; results equal gdr_chunk_fwd's bit for
+ * bit.  No call here allocates or frees memory: the array's device address
+ * is looked up once per device on that device's first call.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Nothing in the array needs clearing between calls: each call
+ * writes every byte it reads. */
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const float* initial_state,
+                                 void* o, float* final_state,
+                                 void* stream);
 
 /* Stage 1 alone (sec-03 notes: in-chunk cumsum, decayed dot, triangular
  * system; UT transform): fills the workspace for gdr_chunk_scan.  With the

@@ -350,3 +350,30 @@ def test_binding_checks_outputs_and_workspace(lib):
         gdr.gdr_decode_step(*dargs, st, out=(torch.empty(1, 4, 64), st.double()))
     with pytest.raises(ValueError, match="on a GPU"):
         gdr.gdr_decode_step(*dargs, st, out=(torch.empty(1, 4, 64), st))
+
+
+def call_noalloc(lib, prob, q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, s0=None,
+                 o=6 * A, sT=7 * A):
+    return lib.gdr_chunk_fwd_noalloc(ctypes.byref(prob), q, k, v, g, beta, s0, o, sT, None)
+
+
+def test_noalloc_validation(lib):
+    """gdr_chunk_fwd_noalloc validates like gdr_chunk_fwd, and refuses a
+    problem whose workspace exceeds the built-in scratch array before any
+    device call."""
+    name = lambda st: binding.STATUS_NAMES[st]
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"#define\s+GDR_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+    assert lib.gdr_chunk_fwd_noalloc(None, *([A] * 8), None) == 1            # GDR_ERR_NULL
+    assert name(call_noalloc(lib, base(B=0))) == "GDR_ERR_SHAPE"
+    assert name(call_noalloc(lib, base(), q=None)) == "GDR_ERR_NULL"
+    assert name(call_noalloc(lib, base(), v=3 * A + 4)) == "GDR_ERR_ALIGN"
+    assert name(call_noalloc(lib, base(), o=A)) == "GDR_ERR_ALIAS"
+    assert name(call_noalloc(lib, base(), sT=2 * A)) == "GDR_ERR_ALIAS"
+    big = base(B=2, T=16000, H=16, HV=32)
+    assert gdr.workspace_size(big) > binding.NOALLOC_SCRATCH_BYTES
+    assert name(call_noalloc(lib, big)) == "GDR_ERR_SCRATCH"
+    assert gdr.status_string(11).startswith("GDR_ERR_SCRATCH")
+    # the 4096-token, 12-head problem fits
+    assert gdr.workspace_size(base(T=4096, H=12, HV=12)) <= binding.NOALLOC_SCRATCH_BYTES
