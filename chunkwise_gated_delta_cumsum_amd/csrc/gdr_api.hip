@@ -84,11 +84,12 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDR_ERR_ARG;
   if (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) return GDR_ERR_ARG;
   if (!std::isfinite(p->scale)) return GDR_ERR_ARG;
-  if (p->chunk != kChunk) return GDR_ERR_UNSUPPORTED;
+  if (p->chunk != 64 && p->chunk != 128) return GDR_ERR_UNSUPPORTED;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
   Prob r;
   r.B = p->B; r.T = p->T; r.H = p->H; r.HV = p->HV; r.K = p->K; r.V = p->V;
-  r.N = (p->T + kChunk - 1) / kChunk;
+  r.C = p->chunk;
+  r.N = (p->T + r.C - 1) / r.C;
   r.perch = p->g_per_channel == 1;
   r.f32 = p->qkv_dtype == GDR_F32;
   r.scale = p->scale;
@@ -98,6 +99,10 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.obf16 = p->o_dtype == GDR_BF16;
   if (p->scan_segments < 0) return GDR_ERR_ARG;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
+  // 128-row chunks are built with one slab width per key dimension: 32
+  // columns for K = 128 (8 waves), 64 for K = 64 (4 waves)
+  const int bv128 = r.K == 128 ? 32 : 64;
+  if (r.C == 128 && p->scan_slab != 0 && p->scan_slab != bv128) return GDR_ERR_UNSUPPORTED;
   // The automatic width: 64 columns, or 32 where the cost model prices them
   // at least 15% cheaper.  The model overrates the narrow slabs by about 10%
   // when few workgroups run: on the 4096-token, 12-head workload it prices
@@ -106,9 +111,10 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   // faster.  Both widths were measured only with 16-bit operands,
   // K = V = 128 and the delta rule (the linear rule's 64-column kernel is a
   // faster instantiation of its own), so elsewhere the choice stays at 64.
-  const bool try32 = p->scan_slab == 0 && !r.f32 && !r.linear && r.K == 128 && r.V == 128;
+  const bool try32 =
+      p->scan_slab == 0 && r.C == 64 && !r.f32 && !r.linear && r.K == 128 && r.V == 128;
   const int BH = r.B * r.HV;
-  r.bv = p->scan_slab != 0 ? p->scan_slab : 64;
+  r.bv = r.C == 128 ? bv128 : (p->scan_slab != 0 ? p->scan_slab : 64);
   if (p->scan_segments == 0) {
     double cost = 0.0, cost32 = 0.0;
     int len32 = 0;
@@ -141,7 +147,7 @@ WsLayout layout(const Prob& r) {
   // q/k fragments: per value head with the per-channel decay folded in, per
   // query head (shared by its value heads) with one decay per row
   const size_t qk = r.perch ? nchunks(r) : (size_t)r.B * r.H * r.N;
-  return ws_layout(nchunks(r), qk, r.K, r.V, r.es, (size_t)r.B * r.HV, r.nseg);
+  return ws_layout(nchunks(r), qk, r.C, r.K, r.V, r.es, (size_t)r.B * r.HV, r.nseg);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -202,6 +208,7 @@ gdr_status check_device() {
 }
 
 gdr_status launch_scan(const Prob& r, ScanArgs& a, hipStream_t s) {
+  if (r.C == 128) return r.f32 ? launch_scan128_f32(r, a, s) : launch_scan128_f16(r, a, s);
   if (r.f32) return launch_scan_f32(r, a, s);
   if (r.linear && r.bv == 64) return launch_scan_f16_linear(r, a, s);
   return launch_scan_f16(r, a, s);
@@ -431,10 +438,10 @@ gdr_status gdr_chunk_prep(const gdr_problem* p, const void* q, const void* k, co
                         workspace_bytes);
   if (out_overlaps(s.ws, {s.q, s.k, s.g, s.beta})) return GDR_ERR_ALIAS;
   const size_t nc = nchunks(r);
-  const Span dg = {gamma, nc * kChunk * (r.perch ? r.K : 1) * sizeof(float)};
-  const Span dm = {a_kk, nc * kChunk * kChunk * sizeof(float)};
-  const Span da = {a_qk, nc * kChunk * kChunk * sizeof(float)};
-  const Span di = {m_inv, nc * kChunk * kChunk * sizeof(float)};
+  const Span dg = {gamma, nc * r.C * (r.perch ? r.K : 1) * sizeof(float)};
+  const Span dm = {a_kk, nc * r.C * r.C * sizeof(float)};
+  const Span da = {a_qk, nc * r.C * r.C * sizeof(float)};
+  const Span di = {m_inv, nc * r.C * r.C * sizeof(float)};
   for (const Span& out : {dg, dm, da, di})
     if (out_overlaps(out, {s.q, s.k, s.g, s.beta, s.ws})) return GDR_ERR_ALIAS;
   if (overlap(dg, dm) || overlap(dg, da) || overlap(dg, di) || overlap(dm, da) ||
@@ -477,7 +484,7 @@ const char* gdr_status_string(int status) {
     case GDR_ERR_NULL: return "GDR_ERR_NULL: a required pointer is NULL";
     case GDR_ERR_SHAPE: return "GDR_ERR_SHAPE: B, T, H, HV, K, V must be >= 1 and HV % H == 0";
     case GDR_ERR_DTYPE: return "GDR_ERR_DTYPE: qkv_dtype must be GDR_F32 or GDR_BF16";
-    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: built for chunk 64 and K, V in {64, 128}";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED: built for chunk 64 or 128 and K, V in {64, 128}; chunk 128 takes scan_slab 0 or its one width (32 for K = 128, 64 for K = 64)";
     case GDR_ERR_ALIGN: return "GDR_ERR_ALIGN: tensors and workspace must be 16-byte aligned";
     case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE: workspace NULL or smaller than gdr_chunk_fwd_workspace_size";
     case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE: the current HIP device is not gfx950";

@@ -40,7 +40,9 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunk = 64;
+// Chunk lengths the kernels are built for.  Every tiling works on 16-row
+// blocks of the chunk, one block per prep wave.
+constexpr int kChunkMin = 64, kChunkMax = 128;
 
 // Barrier for LDS traffic only: wait for this wave's LDS operations, then
 // the workgroup barrier.  No kernel here reads global memory that another
@@ -358,15 +360,17 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 }
 
 // ---- workspace layout -----------------------------------------------------
-// Per chunk (one value head, C = 64 rows), in fragment order so every lane
-// reads or writes 8 consecutive elements:
+// Per chunk (one value head, C = 64 or 128 rows), in fragment order so every
+// lane reads or writes 8 consecutive elements:
 //   wt : W^ = M^-T diag(beta exp(gamma_last - gamma)) k   as the A operand of
-//        W^T (rows d, k = c): [K/16 row tiles][2 k-blocks][64 lanes][8]
-//   ah : A^ = A_qk M^-1 as an A operand (rows i, k = c): [4][2][64][8]
-//   rs : 256 fp32: [0..63] exp(gamma_c) (one decay per row; 1 per channel),
-//        [64..64+K) exp(gamma_last) per key channel
+//        W^T (rows d, k = c): [K/16 row tiles][C/32 k-blocks][64 lanes][8]
+//   ah : A^ = A_qk M^-1 as an A operand (rows i, k = c), lower triangular:
+//        only the k-blocks kb <= I/2 of row tile I are stored, in order
+//        (ah_frag below), [C/16 (C/32 + 1) / 4 ... ][64][8]
+//   rs : 256 fp32: [0..C) exp(gamma_c) (one decay per row; 1 per channel),
+//        [C..C+K) exp(gamma_last) per key channel (C + K <= 256)
 //   qh, kh : the scan's q and k operands as A fragments (rows c, k = d):
-//        [4][K/32][64][8] per chunk; lane (r, g) of fragment (ct, kb) holds
+//        [C/16][K/32][64][8] per chunk; lane (r, g) of fragment (ct, kb) holds
 //        key channels 32 kb + 8 g .. +7 of row 16 ct + r.  Per channel they
 //        are q exp(gamma) scale and k exp(gamma), one per value-head chunk;
 //        with one decay per row they are q and k themselves, converted to
@@ -382,17 +386,26 @@ struct WsLayout {
 
 __host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Fragments of A^ per chunk (the lower-triangular k-blocks), and the index of
+// fragment (row tile I, k-block kb <= I / 2) among them.
+__host__ __device__ constexpr int ah_frags(int C) {
+  return (C / 16) * (C / 16 + 2) / 4;   // sum over I of (I / 2 + 1)
+}
+__host__ __device__ constexpr int ah_frag(int I, int kb) {
+  return (I / 2) * (I / 2 + 1) + (I & 1) * (I / 2 + 1) + kb;
+}
+
 // nchunks = B * HV * N value-head chunks; qkchunks = chunks that carry their
 // own q/k fragments (B * H * N with one decay per row, nchunks per channel).
-__host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, int K, int V,
-                                              size_t elem, size_t nheads, int nseg) {
+__host__ __device__ inline WsLayout ws_layout(size_t nchunks, size_t qkchunks, int C, int K,
+                                              int V, size_t elem, size_t nheads, int nseg) {
   WsLayout L;
   size_t off = 0;
-  L.wt = off; off = ws_align(off + nchunks * (size_t)K * kChunk * elem);
-  L.ah = off; off = ws_align(off + nchunks * (size_t)kChunk * kChunk * elem);
+  L.wt = off; off = ws_align(off + nchunks * (size_t)K * C * elem);
+  L.ah = off; off = ws_align(off + nchunks * (size_t)ah_frags(C) * 512 * elem);
   L.rs = off; off = ws_align(off + nchunks * 256 * sizeof(float));
-  L.qh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
-  L.kh = off; off = ws_align(off + qkchunks * (size_t)kChunk * K * elem);
+  L.qh = off; off = ws_align(off + qkchunks * (size_t)C * K * elem);
+  L.kh = off; off = ws_align(off + qkchunks * (size_t)C * K * elem);
   L.phi = L.eend = L.s0c = off;
   if (nseg > 1) {
     L.phi = off; off = ws_align(off + nheads * (nseg - 1) * (size_t)K * K * elem);

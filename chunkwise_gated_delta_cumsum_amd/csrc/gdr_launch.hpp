@@ -1,7 +1,8 @@
 // Kernel launchers of the library, shared by gdr_api.hip (the host logic of
 // the C ABI) and the launcher translation units, one per kernel family
-// (gdr_launch_prep.hip, gdr_launch_scan_f16.hip, gdr_launch_scan_lin.hip,
-// gdr_launch_scan_f32.hip, gdr_launch_decode.hip), which instantiate the
+// (gdr_launch_prep.hip, gdr_launch_prep128.hip, gdr_launch_scan_f16.hip,
+// gdr_launch_scan_lin.hip, gdr_launch_scan_f32.hip, gdr_launch_scan128_f16.hip,
+// gdr_launch_scan128_f32.hip, gdr_launch_decode.hip), which instantiate the
 // kernels and compile in parallel.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -16,6 +17,7 @@ namespace gdr {
 // A validated problem (see validate in gdr_api.hip).
 struct Prob {
   int B, T, H, HV, K, V, N;
+  int C;             // chunk length, 64 or 128
   bool perch, f32;
   float scale;
   size_t es;        // bytes per q/k/v element and per workspace fragment element
@@ -36,9 +38,12 @@ inline gdr_status launch(Kern kern, unsigned grid, unsigned block, Args& args, h
 
 // Both stages and the decode step, on the caller's stream.
 gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s);
+gdr_status launch_prep128(const Prob& r, PrepArgs& a, bool dump, hipStream_t s);
 gdr_status launch_scan_f16(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan_f16_linear(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan_f32(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_scan128_f16(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_scan128_f32(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_decode(int K, int V, int vb, bool perch, bool f32, DecodeArgs& a,
                          hipStream_t s);
 

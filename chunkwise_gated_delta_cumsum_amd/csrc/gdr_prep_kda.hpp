@@ -5,6 +5,7 @@
 // into their operands, exp(gamma_i - gamma_j) = f(i) f'(j) per channel, with
 // every factor kept in range.
 //
+// One wave per 16-row block (NB = C / 16 waves for C = 64 or 128 rows).
 // Wave I owns the rows of block I (rows 16I..16I+15); lane (r, grp) holds row
 // 16I + r at channels 8grp .. 8grp+7 of every 32-channel group (fragment
 // slot i holds channel 8grp + i: the state's key-channel order, see
@@ -25,7 +26,7 @@
 //      wave sums the 16x16 entries explicitly, exp per channel and entry.
 //   4. q exp(gamma) scale and k exp(gamma) (the scan's operands) and
 //      beta k exp(gamma_last - gamma) (for W^) from the same factors and the
-//      per-block tables exp(pre[I]) and exp(pre[4] - pre[I+1]).
+//      per-block tables exp(pre[I]) and exp(pre[NB] - pre[I+1]).
 // Steps 3-4 of the UT transform (inverse and folding) are shared with the
 // scalar kernel.  With g > 0 the factors grow as exp(sum of the positive g in
 // the chunk); fp16 operands stay finite while that sum is below about 8.
@@ -52,23 +53,25 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
-template <int K, class P, bool DUMP>
-__global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
+template <int K, int C, class P, bool DUMP>
+__global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
   using ws_t = typename P::ws_t;
   using raw_t = typename P::raw_t;
-  constexpr int C = kChunk;
+  constexpr int NB = C / 16;                        // waves, one 16-row block each
+  constexpr int NT = NB * 64;
   constexpr int KB = K / 32;
-  constexpr int LP = kLP;
+  constexpr int LP = lds_ld<C>();
   constexpr int SP = K + 16 / (int)sizeof(ws_t);   // row of the W^ operand tile, +16 bytes
-  constexpr int NPAIR = 6;                          // off-diagonal block pairs J < I
+  constexpr int NPAIR = NB * (NB - 1) / 2;          // off-diagonal block pairs J < I
 
-  constexpr size_t KE_BYTES = (size_t)3 * KB * 64 * sizeof(frag_t);
-  constexpr size_t TAB_BYTES = (size_t)(4 + 4 + NPAIR) * K * sizeof(float);
-  constexpr size_t MT_BYTES = (size_t)C * LP * sizeof(float);
-  constexpr size_t X_BYTES = KE_BYTES + TAB_BYTES > MT_BYTES ? KE_BYTES + TAB_BYTES : MT_BYTES;
+  constexpr size_t KE_BYTES = (size_t)(NB - 1) * KB * 64 * sizeof(frag_t);
+  constexpr size_t TAB_BYTES = (size_t)(NB + NB + NPAIR) * K * sizeof(float);
   constexpr size_t SK_BYTES = (size_t)C * SP * sizeof(ws_t);
+  // the W^ operand tile takes the bytes of the earlier-row fragments and the
+  // tables once they are dead
+  constexpr size_t X_BYTES = KE_BYTES + TAB_BYTES > SK_BYTES ? KE_BYTES + TAB_BYTES : SK_BYTES;
   constexpr size_t L_BYTES = (size_t)C * LP * sizeof(float);
   // Loads: each wave's 16 rows of g, q and k arrive as whole rows (16 bytes
   // per lane, a row per 16..32 lanes) and pass through a per-wave staging
@@ -79,23 +82,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   constexpr int GSR = K * 4 + 16;                           // staged g row (bytes)
   constexpr int QSR = K * (int)sizeof(in_t) + 16;           // staged q / k row
   constexpr int STG = 16 * GSR > 32 * QSR ? 16 * GSR : 32 * QSR;
-  static_assert(4 * (size_t)STG <= X_BYTES + SK_BYTES + L_BYTES, "staging fits the LDS block");
+  constexpr size_t BIG = NB * (size_t)STG > X_BYTES + L_BYTES ? NB * (size_t)STG
+                                                               : X_BYTES + L_BYTES;
+  static_assert(NB * 512 * sizeof(float) <= L_BYTES, "diagonal scratch fits the A_kk tile");
   // one LDS block, in phases: the load staging first; then sX = earlier-row
-  // fragments of blocks 0..2 and the per-channel tables (M^-T later), sSK =
-  // beta k exp(gamma_last - gamma), row-major (c, d), for W^, and sL = A_kk
-  // beta (strict; D_I later)
-  __shared__ __attribute__((aligned(16))) char sBig[X_BYTES + SK_BYTES + L_BYTES];
+  // fragments of blocks 0..NB-2 and the per-channel tables, later sSK =
+  // beta k exp(gamma_last - gamma), row-major (c, d), for W^; and sL = A_kk
+  // beta (strict; D_I later, M^-T after the inverse)
+  __shared__ __attribute__((aligned(16))) char sBig[BIG];
   char* sX = sBig;
-  ws_t* sSK = reinterpret_cast<ws_t*>(sBig + X_BYTES);
-  float* sL = reinterpret_cast<float*>(sBig + X_BYTES + SK_BYTES);
-  __shared__ __attribute__((aligned(16))) float sTot[4 * K];   // s at row 15 of each block
-  __shared__ __attribute__((aligned(16))) float sMid[4 * K];   // s at row 7 of each block
+  ws_t* sSK = reinterpret_cast<ws_t*>(sBig);
+  float* sL = reinterpret_cast<float*>(sBig + X_BYTES);
+  __shared__ __attribute__((aligned(16))) float sTot[NB * K];  // s at row 15 of each block
+  __shared__ __attribute__((aligned(16))) float sMid[NB * K];  // s at row 7 of each block
   __shared__ float sBeta[C];
-  frag_t* sKE = reinterpret_cast<frag_t*>(sX);                  // [3][KB][64]
-  float* sPf = reinterpret_cast<float*>(sX + KE_BYTES);         // [4][K] exp(pre[I])
-  float* sSf = sPf + 4 * K;                                      // [4][K] exp(pre[4] - pre[I+1])
-  float* sCf = sSf + 4 * K;                                      // [6][K] exp(pre[I] - pre[J+1])
-  float* sMT = reinterpret_cast<float*>(sX);
+  frag_t* sKE = reinterpret_cast<frag_t*>(sX);                  // [NB-1][KB][64]
+  float* sPf = reinterpret_cast<float*>(sX + KE_BYTES);         // [NB][K] exp(pre[I])
+  float* sSf = sPf + NB * K;                                     // [NB][K] exp(pre[NB] - pre[I+1])
+  float* sCf = sSf + NB * K;                                     // [NPAIR][K] exp(pre[I] - pre[J+1])
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r = lane & 15, grp = lane >> 4;
@@ -207,24 +211,30 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   // ---- per-channel tables (all threads) --------------------------------------
   {
     const int d = tid % K, part = tid / K;
-    float pre[5];
-    pre[0] = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) pre[m + 1] = pre[m] + sTot[m * K + d];
+    // pre[m] = sum of the block totals before block m, in the order m = 0, 1, ...
+    auto pre = [&](int m) {
+      float x = 0.f;
+      for (int j = 0; j < m; ++j) x += sTot[j * K + d];
+      return x;
+    };
     float* rs = a.rs + (size_t)cid * 256;
-    for (int it = part; it < 15; it += 256 / K) {
-      if (it < 4) {
-        sPf[it * K + d] = __expf(pre[it]);
-      } else if (it < 8) {
-        sSf[(it - 4) * K + d] = __expf(pre[4] - pre[it - 3]);
-      } else if (it < 14) {
-        const int p = it - 8, I2 = p < 1 ? 1 : (p < 3 ? 2 : 3), J2 = p - I2 * (I2 - 1) / 2;
-        sCf[p * K + d] = __expf(pre[I2] - pre[J2 + 1]);
+    for (int it = part; it < 2 * NB + NPAIR + 1; it += NT / K) {
+      if (it < NB) {
+        sPf[it * K + d] = __expf(pre(it));
+      } else if (it < 2 * NB) {
+        sSf[(it - NB) * K + d] = __expf(pre(NB) - pre(it - NB + 1));
+      } else if (it < 2 * NB + NPAIR) {
+        // pair p = I2 (I2 - 1) / 2 + J2 with J2 < I2
+        const int p = it - 2 * NB;
+        int I2 = 1;
+        while ((I2 + 1) * I2 / 2 <= p) ++I2;
+        const int J2 = p - I2 * (I2 - 1) / 2;
+        sCf[p * K + d] = __expf(pre(I2) - pre(J2 + 1));
       } else {
-        rs[64 + row_of_chan(d)] = __expf(pre[4]);   // in the state's row order
+        rs[C + row_of_chan(d)] = __expf(pre(NB));   // in the state's row order
       }
     }
-    if (tid < C) rs[tid] = 1.f;
+    for (int e = tid; e < C; e += NT) rs[e] = 1.f;
   }
 
   // ---- 2/3. own-block factors, earlier-row fragments, diagonal tiles ----------
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       b1[j] = kv * dmi;
       b2[j] = qv * dm;
     }
-    if (I < 3) sKE[(I * KB + kb) * 64 + lane] = P::make(ke[kb]);
+    if (I < NB - 1) sKE[(I * KB + kb) * 64 + lane] = P::make(ke[kb]);
     const f32x8 fa1 = {a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]};
     const f32x8 fb1 = {b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]};
     const f32x8 fb2 = {b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]};
@@ -268,9 +278,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   if (__any(far)) {
     // Explicit diagonal block: lane (r, grp) sums its channels for the pairs
     // (row r, row (r - m) mod 16), m = 0..15, the four channel groups are
-    // added across lanes, and the entries are routed through LDS (the W^
+    // added across lanes, and the entries are routed through LDS (the A_kk
     // tile is not written yet) into accumulator layout.
-    float* scr = reinterpret_cast<float*>(sSK) + wave * 512;   // [2][16][16]
+    float* scr = sL + wave * 512;   // [2][16][16]
     for (int m = 0; m < 16; ++m) {
       const int jr = (r - m) & 15;
       const int src = jr + 16 * grp;
@@ -323,9 +333,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   GDR_PPROF(2);
 
   // ---- off-diagonal tiles (J < I) ----------------------------------------------
-  f32x4 aqT[4];
+  f32x4 aqT[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) aqT[j] = zero4();
+  for (int j = 0; j < NB; ++j) aqT[j] = zero4();
   if (I > 0) {
     frag_t kLf[KB], qLf[KB];
 #pragma unroll
@@ -366,8 +376,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
   }
 
   // ---- scan operands and the W^ operand ----------------------------------------
+  // (the W^ operand rows stay in registers until the tables are dead: their
+  // LDS tile takes the tables' bytes)
+  float wx[KB][8];
   {
-    const size_t off0 = (size_t)cid * 4 * KB * 512 + ((size_t)I * KB) * 512 + lane * 8;
+    const size_t off0 = (size_t)cid * NB * KB * 512 + ((size_t)I * KB) * 512 + lane * 8;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int d0 = 32 * kb + 8 * grp;
@@ -375,40 +388,49 @@ __global__ __launch_bounds__(256) void chunk_prep_kda_kernel(PrepArgs a) {
       const f32x4 pb = *reinterpret_cast<const f32x4*>(sPf + I * K + d0 + 4);
       const f32x4 wa = *reinterpret_cast<const f32x4*>(sSf + I * K + d0);
       const f32x4 wb = *reinterpret_cast<const f32x4*>(sSf + I * K + d0 + 4);
-      float qx[8], kx[8], wx[8];
+      float qx[8], kx[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float pf = j < 4 ? pa[j] : pb[j - 4];     // exp(gamma_i) = exp(s) exp(pre[I])
         qx[j] = ql[kb][j] * pf * a.scale;
         kx[j] = kl[kb][j] * pf;
-        // exp(gamma_last - gamma_i) = exp(s15 - s) exp(pre[4] - pre[I+1])
-        wx[j] = bv * ke[kb][j] * (j < 4 ? wa[j] : wb[j - 4]);
+        // exp(gamma_last - gamma_i) = exp(s15 - s) exp(pre[NB] - pre[I+1])
+        wx[kb][j] = bv * ke[kb][j] * (j < 4 ? wa[j] : wb[j - 4]);
       }
       store_ws8(static_cast<ws_t*>(a.qh) + off0 + (size_t)kb * 512, qx);
       store_ws8(static_cast<ws_t*>(a.kh) + off0 + (size_t)kb * 512, kx);
-      store_ws4(sSK + i * SP + d0, wx);
-      store_ws4(sSK + i * SP + d0 + 4, wx + 4);
     }
   }
-  lds_barrier();   // sL and sSK complete; sKE and the tables are dead
+  lds_barrier();   // sL complete; sKE and the tables are dead
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    store_ws4(sSK + i * SP + 32 * kb + 8 * grp, wx[kb]);
+    store_ws4(sSK + i * SP + 32 * kb + 8 * grp + 4, wx[kb] + 4);
+  }
+  lds_barrier();   // sSK complete
   GDR_PPROF(3);
 
   if constexpr (DUMP) {
-    if (a.d_akk) dump_akk(a.d_akk + (size_t)cid * C * C, sL, tid);
-    if (a.d_aqk) dump_aqk(a.d_aqk + (size_t)cid * C * C, aqT, wave, r, grp);
+    if (a.d_akk) dump_akk<C>(a.d_akk + (size_t)cid * C * C, sL, tid);
+    if (a.d_aqk) dump_aqk<C>(a.d_aqk + (size_t)cid * C * C, aqT, wave, r, grp);
+    lds_barrier();   // sL is read before the inverse overwrites it
   }
 
-  // ---- M^-1, then the folded operands ------------------------------------------
-  unit_lower_inverse<P>(sL, sMT, tid, wave, r, grp);
+  // ---- M^-1 (M^-T replaces A_kk in sL), then the folded operands -------------
+  if (a.linear)
+    identity_inverse<C>(sL, tid);
+  else
+    unit_lower_inverse<C, P>(sL, wave, r, grp);
   GDR_PPROF(4);
   if constexpr (DUMP) {
-    if (a.d_minv) dump_minv(a.d_minv + (size_t)cid * C * C, sMT, tid);
+    if (a.d_minv) dump_minv<C>(a.d_minv + (size_t)cid * C * C, sL, tid);
   }
-  fold_w<K, P, false>(sMT, static_cast<ws_t*>(a.wt) + (size_t)cid * K * C, wave, lane, r, grp,
-                      [&](int c, int d) { return (float)sSK[c * SP + d]; },
-                      [&](int) { return 1.f; });
+  fold_w<K, C, P, false>(sL, static_cast<ws_t*>(a.wt) + (size_t)cid * K * C, wave, lane, r, grp,
+                         [&](int c, int d) { return (float)sSK[c * SP + d]; },
+                         [&](int) { return 1.f; });
   GDR_PPROF(5);
-  fold_aqk<P>(aqT, sMT, static_cast<ws_t*>(a.ah) + (size_t)cid * C * C, wave, lane, r, grp);
+  fold_aqk<C, P>(aqT, sL, static_cast<ws_t*>(a.ah) + (size_t)cid * ah_frags(C) * 512, wave,
+                 lane, r, grp);
   GDR_PPROF(6);
   GDR_PPROF_FLUSH;
 }

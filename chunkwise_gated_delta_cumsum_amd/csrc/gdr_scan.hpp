@@ -25,10 +25,10 @@
 //                 (combine_prefix).
 // With one segment only the full mode runs.
 //
-// Work split in a workgroup of NW = 4 waves (BV = 32 or 64 state columns, a
-// "slab"):
-// wave w owns chunk rows [16w, 16w+16) of Y, Z and o and state rows
-// [K/4 w, K/4 (w+1)).  Every A-operand fragment (k, q, W^T and A^ rows)
+// Work split in a workgroup of NW waves (4, or 8 for 128-row chunks with
+// K = 128) over BV = 32 or 64 state columns (a "slab"): wave w owns chunk
+// rows [C/NW w, C/NW (w+1)) of Y, Z and o and state rows [K/NW w,
+// K/NW (w+1)).  Every A-operand fragment (k, q, W^T and A^ rows)
 // belongs to exactly one wave, which loads it straight into registers.  The
 // next chunk's operands are double-buffered and their loads are issued one
 // at a time between the current chunk's products: issued in a burst they
@@ -87,13 +87,13 @@ struct ScanArgs {
 #ifdef GDR_SCAN_PROFILE
 // clock marks of one chunk step, kept in registers and written out at the
 // end of the step (a store per mark would add waits of its own)
-__device__ long long gdr_scan_prof[64 * 16 * 4];
+__device__ long long gdr_scan_prof[64 * 16 * 8];
 #define GDR_PROF_DECL long long pt_[16] = {}
 #define GDR_PROF(ph) pt_[ph] = clock64()
 #define GDR_PROF_FLUSH                                                             \
   do {                                                                             \
     if (MODE == kScanFull && bh == 0 && p == 0 && sv == 0 && lane == 0 && n < 64)   \
-      for (int i_ = 0; i_ < 16; ++i_) gdr_scan_prof[(n * 16 + i_) * 4 + w] = pt_[i_]; \
+      for (int i_ = 0; i_ < 16; ++i_) gdr_scan_prof[(n * 16 + i_) * 8 + w] = pt_[i_]; \
   } while (0)
 #else
 #define GDR_PROF_DECL do {} while (0)
@@ -103,7 +103,12 @@ __device__ long long gdr_scan_prof[64 * 16 * 4];
 
 constexpr int kScanFull = 0;
 constexpr int kScanChain = 1;
-constexpr int kScanWaves = 4;
+
+// Waves per scan workgroup: one 16-row tile of the chunk and K/16/NW state
+// row tiles each; 128-row chunks with K = 128 take 8 waves (one chunk row
+// tile and one state row tile each), everything else 4.
+template <int K, int C>
+constexpr int scan_waves() { return (C == 128 && K == 128) ? 8 : 4; }
 
 
 // Calls f(std::integral_constant<int, I>{}) for I = B .. E-1.
@@ -148,9 +153,9 @@ __device__ __forceinline__ size_t state_tile(int sv, int dt, int ct) {
 }
 
 // Bytes of one wave's staging area for its fp32 o rows (full mode only).
-template <int MODE, int BV>
+template <int MODE, int BV, int C, int NW>
 constexpr int scan_stage_bytes() {
-  return MODE == kScanFull ? (kChunk / kScanWaves) * (BV * 4 + 16) : 16;
+  return MODE == kScanFull ? (C / NW) * (BV * 4 + 16) : 16;
 }
 
 // The start state of segment p from the chain pass's results:
@@ -227,7 +232,8 @@ __device__ __forceinline__ void combine_prefix(const ScanArgs& a, typename P::fr
 // One wave of a scan workgroup.  W (the wave index) and PHI (chain mode:
 // transition slab, identity start and no v) are template arguments so that
 // every choice between waves and slab kinds folds at compile time.
-template <int K, int V, bool PERCH, class P, int MODE, int BV, int NW, int W, bool PHI, bool LIN>
+template <int K, int V, bool PERCH, class P, int MODE, int BV, int C, int NW, int W, bool PHI,
+          bool LIN>
 __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t* sS,
                                           typename P::frag_t* sZ, typename P::in_t* sVw,
                                           unsigned char* stg, int unit, int sv) {
@@ -235,13 +241,14 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   using frag_t = typename P::frag_t;
   using ws_t = typename P::ws_t;
   constexpr bool FULL = MODE == kScanFull;
-  constexpr int C = kChunk;
   constexpr int NCT = BV / 16;     // column tiles
   constexpr int KT = K / 16;       // state row tiles
   constexpr int KB = K / 32;       // 32-wide k blocks over K
+  constexpr int CB = C / 32;       // 32-wide k blocks over the chunk rows
   constexpr int SRT = KT / NW;     // state row tiles per wave
-  constexpr int CT = 4 / NW;       // chunk row tiles per wave
+  constexpr int CT = C / 16 / NW;  // chunk row tiles per wave
   constexpr int CR = 16 * CT;      // chunk rows per wave
+  static_assert(SRT * NW == KT && CT * NW == C / 16, "scan wave split");
   constexpr int VVEC = 16 / (int)sizeof(in_t);       // v elements per 16 bytes
   constexpr int VPR = BV / VVEC;                     // 16-byte pieces per v row
   constexpr int VRI = 64 / VPR;                      // v rows per load instruction
@@ -283,7 +290,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   u32x4 vr[VNI];
   struct WA {
     frag_t kf[CT][KB], qf[CT][KB];
-    frag_t wf[SRT][2], af[CT][2];
+    frag_t wf[SRT][CB], af[CT][AKB];
     f32x4 eg[CT];                        // exp(gamma), rows CR w + 16ct + 4grp + j
     float ego[CT];                       // exp(gamma), row CR w + 16ct + r
     f32x4 dl[PERCH ? SRT : 1];           // exp(gamma_last) per state row (one value
@@ -295,7 +302,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   // columns of A^ (beta = 0 there), and their o is not stored.
   const size_t qkb = PERCH ? (size_t)bh * a.N : ((size_t)b * a.H + h) * a.N;
   auto kq_load = [&](const ws_t* wsb, int n, int ct, int kb) -> frag_t {
-    return frag_ws(wsb + (((qkb + n) * 4 + CT * w + ct) * KB + kb) * 512 + lane * 8);
+    return frag_ws(wsb + (((qkb + n) * (C / 16) + CT * w + ct) * KB + kb) * 512 + lane * 8);
   };
   auto load_v = [&](int n) {
     if constexpr (!PHI) {
@@ -315,7 +322,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   constexpr int IT_K = 0;
   constexpr int IT_Q = IT_K + (LIN ? 0 : NKQ);  // the linear rule never reads k here
   constexpr int IT_W = IT_Q + (FULL ? NKQ : 0);
-  constexpr int IT_A = IT_W + ((LIN && PHI) ? 0 : SRT * 2);
+  constexpr int IT_A = IT_W + ((LIN && PHI) ? 0 : SRT * CB);
   constexpr int IT_R = IT_A + (FULL ? CT * AKB : 0);
   constexpr int NITEMS = IT_R + 1;
   auto load_item = [&](int i, int n, WA& x) {
@@ -330,20 +337,21 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
         x.qf[ct][kb] = kq_load(static_cast<const ws_t*>(a.qh), n, ct, kb);
       }
     } else if (i < IT_A) {
-      const int st = (i - IT_W) / 2, kb = (i - IT_W) % 2;
-      x.wf[st][kb] = frag_ws(wtg + ((cid * KT + SRT * w + st) * 2 + kb) * 512 + lane * 8);
+      const int st = (i - IT_W) / CB, kb = (i - IT_W) % CB;
+      x.wf[st][kb] = frag_ws(wtg + ((cid * KT + SRT * w + st) * CB + kb) * 512 + lane * 8);
     } else if (i < IT_R) {
       if constexpr (FULL) {
         const int ct = (i - IT_A) / AKB, kb = (i - IT_A) % AKB;
-        x.af[ct][kb] = frag_ws(ahg + ((cid * 4 + CT * w + ct) * 2 + kb) * 512 + lane * 8);
+        x.af[ct][kb] = frag_ws(ahg + (cid * ah_frags(C) + ah_frag(CT * w + ct, kb)) * 512 +
+                               lane * 8);
       }
     } else {
       if constexpr (PERCH) {
 #pragma unroll
         for (int st = 0; st < SRT; ++st)
-          x.dl[st] = *reinterpret_cast<const f32x4*>(rs + 64 + 16 * (SRT * w + st) + 4 * grp);
+          x.dl[st] = *reinterpret_cast<const f32x4*>(rs + C + 16 * (SRT * w + st) + 4 * grp);
       } else {
-        x.dl[0][0] = rs[64];
+        x.dl[0][0] = rs[C];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           x.eg[ct] = *reinterpret_cast<const f32x4*>(rs + CR * w + 16 * ct + 4 * grp);
@@ -406,7 +414,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   // them with the state: one barrier per step instead of two, and no Y.
   auto publish_vz = [&](int n) {
     if constexpr (LIN && !PHI) {
-      frag_t* zb = sZ + (n & 1) * (2 * NCT * 64);
+      frag_t* zb = sZ + (n & 1) * (CB * NCT * 64);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -552,22 +560,16 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
     float sc[CT];
 #pragma unroll
     for (int c2 = 0; c2 < CT; ++c2) sc[c2] = (FULL && !PERCH) ? cur.ego[c2] * a.scale : 1.f;
-    frag_t bZ[2][NCT];
-    const frag_t* zr = LIN ? sZ + (n & 1) * (2 * NCT * 64) : sZ;
+    frag_t bZ[CB][NCT];
+    const frag_t* zr = LIN ? sZ + (n & 1) * (CB * NCT * 64) : sZ;
     if constexpr (!(LIN && PHI)) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        bZ[0][ct] = zr[(0 * NCT + ct) * 64 + lane];
-        bZ[1][ct] = zr[(1 * NCT + ct) * 64 + lane];
-      }
+      for (int kb = 0; kb < CB; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) bZ[kb][ct] = zr[(kb * NCT + ct) * 64 + lane];
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      frag_t z0 = {}, z1 = {};
-      if constexpr (!(LIN && PHI)) {
-        z0 = bZ[0][ct];
-        z1 = bZ[1][ct];
-      }
 #pragma unroll
       for (int st = 0; st < SRT; ++st) {
         if constexpr (PERCH)
@@ -575,8 +577,8 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
         else
           S[st][ct] *= cur.dl[0][0];
         if constexpr (!(LIN && PHI)) {   // (the linear rule's transition: Z = 0)
-          S[st][ct] = mma32(cur.wf[st][0], z0, S[st][ct]);
-          S[st][ct] = mma32(cur.wf[st][1], z1, S[st][ct]);
+#pragma unroll
+          for (int kb = 0; kb < CB; ++kb) S[st][ct] = mma32(cur.wf[st][kb], bZ[kb][ct], S[st][ct]);
         }
         if (item < NITEMS) load_item(item++, nn, nxt);
         __builtin_amdgcn_sched_barrier(0);
@@ -585,8 +587,9 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
 #pragma unroll
         for (int c2 = 0; c2 < CT; ++c2) {
           if constexpr (!PERCH) OT[ct][c2] *= sc[c2];
-          OT[ct][c2] = mma32(z0, cur.af[c2][0], OT[ct][c2]);
-          if constexpr (AKB > 1) OT[ct][c2] = mma32(z1, cur.af[c2][1], OT[ct][c2]);
+#pragma unroll
+          for (int kb = 0; kb < AKB; ++kb)
+            OT[ct][c2] = mma32(bZ[kb][ct], cur.af[c2][kb], OT[ct][c2]);
         }
       }
     }
@@ -660,21 +663,23 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
   }
 }
 
-template <int K, int V, bool PERCH, class P, int MODE, int BV, bool LIN = false>
-__global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a) {
+template <int K, int V, bool PERCH, class P, int MODE, int BV, int C, bool LIN = false>
+__global__ __launch_bounds__((scan_waves<K, C>() * 64)) void chunk_scan_kernel(ScanArgs a) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
-  constexpr int NW = kScanWaves;
+  constexpr int NW = scan_waves<K, C>();
   constexpr bool FULL = MODE == kScanFull;
   constexpr int NSLAB = FULL ? V / BV : (K + V) / BV;
   constexpr int NCT = BV / 16;
   constexpr int KB = K / 32;
+  constexpr int CB = C / 32;
   constexpr int VVEC = 16 / (int)sizeof(in_t);
   constexpr int VP = BV + VVEC;
   __shared__ frag_t sS[(LIN ? 2 : 1) * KB * NCT * 64];  // B fragments of S (2 buffers: LIN)
-  __shared__ frag_t sZ[(LIN ? 2 : 1) * 2 * NCT * 64];  // B fragments of Z (2 buffers: LIN)
-  __shared__ __attribute__((aligned(16))) in_t sV[NW][(64 / NW) * VP];
-  __shared__ __attribute__((aligned(16))) unsigned char sStg[NW][scan_stage_bytes<MODE, BV>()];
+  __shared__ frag_t sZ[(LIN ? 2 : 1) * CB * NCT * 64];  // B fragments of Z (2 buffers: LIN)
+  __shared__ __attribute__((aligned(16))) in_t sV[NW][(C / NW) * VP];
+  __shared__ __attribute__((aligned(16))) unsigned char
+      sStg[NW][scan_stage_bytes<MODE, BV, C, NW>()];
 
   const int nsegu = FULL ? a.nseg : a.nseg - 1;       // segments handled by this pass
   int unit, sv;
@@ -693,13 +698,12 @@ __global__ __launch_bounds__(kScanWaves * 64) void chunk_scan_kernel(ScanArgs a)
   GDR_WGT(FULL ? 3 : 1, 0);
   auto run = [&](auto phi) {
     constexpr bool PHI = decltype(phi)::value;
-    if (wv == 0) scan_wave<K, V, PERCH, P, MODE, BV, NW, 0, PHI, LIN>(a, sS, sZ, sV[0], sStg[0], unit, sv);
-    if constexpr (NW > 1)
-      if (wv == 1) scan_wave<K, V, PERCH, P, MODE, BV, NW, 1, PHI, LIN>(a, sS, sZ, sV[1], sStg[1], unit, sv);
-    if constexpr (NW > 2) {
-      if (wv == 2) scan_wave<K, V, PERCH, P, MODE, BV, NW, 2, PHI, LIN>(a, sS, sZ, sV[2], sStg[2], unit, sv);
-      if (wv == 3) scan_wave<K, V, PERCH, P, MODE, BV, NW, 3, PHI, LIN>(a, sS, sZ, sV[3], sStg[3], unit, sv);
-    }
+    static_for_scan<0, NW>([&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      if (wv == W)
+        scan_wave<K, V, PERCH, P, MODE, BV, C, NW, W, PHI, LIN>(a, sS, sZ, sV[W], sStg[W], unit,
+                                                                 sv);
+    });
   };
   if (FULL || sv >= K / BV)
     run(std::false_type{});

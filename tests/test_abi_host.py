@@ -81,7 +81,8 @@ def test_workspace_size(lib):
     p = base()
     n = 1 * 4 * 2   # B * HV * ceil(100 / 64)
     nq = 1 * 2 * 2  # B * H * ceil(100 / 64): q and k fragments per query head
-    expect_min = n * (128 * 64 * 2 + 64 * 64 * 2 + 256 * 4) + nq * 2 * (64 * 128 * 2)
+    # per chunk: W^ (K x C), the 6 lower-triangular fragments of A^, row scalars
+    expect_min = n * (128 * 64 * 2 + 6 * 512 * 2 + 256 * 4) + nq * 2 * (64 * 128 * 2)
     assert gdr.workspace_size(p) >= expect_min
     assert gdr.workspace_size(base(per_channel=True)) > gdr.workspace_size(p)
     assert gdr.workspace_size(base(dtype="fp32")) > gdr.workspace_size(p)
@@ -377,3 +378,25 @@ def test_noalloc_validation(lib):
     assert gdr.status_string(11).startswith("GDR_ERR_SCRATCH")
     # the 4096-token, 12-head problem fits
     assert gdr.workspace_size(base(T=4096, H=12, HV=12)) <= binding.NOALLOC_SCRATCH_BYTES
+
+
+def test_chunk_128_problems(lib):
+    """Chunk lengths 64 and 128 are built; 128-row chunks use one slab width
+    per key dimension (32 columns for K = 128, 64 for K = 64)."""
+    name = lambda st: binding.STATUS_NAMES[st]
+    for K, bv in ((128, 32), (64, 64)):
+        p = base(T=1000, K=K, V=128, chunk=128)
+        assert gdr.workspace_size(p) > 0
+        assert gdr.scan_slab(p) == bv
+        assert gdr.scan_slab(base(T=1000, K=K, chunk=128, slab=bv)) == bv
+        other = 64 if bv == 32 else 32
+        assert name(call_fwd(lib, base(T=1000, K=K, chunk=128, slab=other))) == "GDR_ERR_UNSUPPORTED"
+    for C in (32, 96, 256, 0):
+        assert name(call_fwd(lib, base(chunk=C))) == "GDR_ERR_UNSUPPORTED"
+    # the workspace per token: the same W^ and q/k fragments, A^ keeps the
+    # lower-triangular k-blocks (20 of 32 fragments at C = 128, 6 of 8 at 64)
+    w64 = gdr.workspace_size(base(T=4096, H=12, HV=12, segments=1))
+    w128 = gdr.workspace_size(base(T=4096, H=12, HV=12, segments=1, chunk=128))
+    nc = 12 * 64                       # value-head chunks of 64 rows
+    assert w128 - w64 == (nc // 2) * (20 - 2 * 6) * 512 * 2 - (nc // 2) * 256 * 4
+    assert gdr.scan_segments(base(T=4096, H=12, HV=12, chunk=128, segments=3)) == 3
