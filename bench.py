@@ -54,7 +54,8 @@ def traffic_model(w):
     o = tok * w.HV * w.V * 4
     state = w.B * w.HV * w.K * w.V * 4
     s0 = state if w.s0_std > 0 else 0
-    ws = nch * (C * w.K * wes + C * C * wes + (64 + w.K) * 4)
+    ah_frags = (C // 16) * (C // 16 + 2) // 4        # lower-triangular A^ fragments
+    ws = nch * (C * w.K * wes + ah_frags * 512 * wes + 256 * 4)
     qkh = 2 * nch * C * w.K * wes if w.per_channel else 0
     design = dict(chunk_prep=qk + g + beta + ws + qkh,
                   state_scan=(qkh if w.per_channel else qk) + v + ws + s0 + o + state)

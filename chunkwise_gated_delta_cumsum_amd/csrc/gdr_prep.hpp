@@ -73,17 +73,19 @@ __device__ long long gdr_prep_prof[16 * 8];
 #define GDR_PPROF_FLUSH do {} while (0)
 #endif
 
-// XCD-aware placement of chunks: the value heads that share one q/k head get
-// the same (id % 8), so their q/k rows meet in one L2.
+// XCD-aware placement of chunks: workgroups are dealt to the 8 XCDs round
+// robin, so the HV value heads of one (batch, chunk) get the same (id % 8)
+// and consecutive slots: the value heads that share a q/k head read its rows
+// through one L2, and so do all heads reading their g and beta, which share
+// the cache lines of one token ([B, T, HV] rows of HV values).
 __device__ __forceinline__ bool prep_block(int B, int H, int G, int N, int& b, int& hv, int& n) {
   const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
-  const long unit = (long)(slot / G) * 8 + xcd;      // (b, h, n)
-  const int gi = slot % G;
-  if (unit >= (long)B * H * N) return false;
+  const int HV = H * G;
+  const long unit = (long)(slot / HV) * 8 + xcd;     // (b, n)
+  if (unit >= (long)B * N) return false;
+  b = (int)(unit / N);
   n = (int)(unit % N);
-  const long bhq = unit / N;
-  b = (int)(bhq / H);
-  hv = (int)(bhq % H) * G + gi;
+  hv = slot % HV;
   return true;
 }
 

@@ -7,10 +7,10 @@ namespace gdr {
 
 template <int K, int C, bool PERCH, class P>
 gdr_status launch_prep_k(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
-  // (batch, q/k head, chunk) units rounded up to the 8 XCDs, times the
-  // value heads of each q/k head; surplus workgroups exit
-  const size_t units8 = ((size_t)r.B * r.H * r.N + 7) / 8 * 8;
-  const unsigned grid = (unsigned)(units8 * (r.HV / r.H));
+  // (batch, chunk) units rounded up to the 8 XCDs, times the value heads;
+  // surplus workgroups exit (see prep_block)
+  const size_t units8 = ((size_t)r.B * r.N + 7) / 8 * 8;
+  const unsigned grid = (unsigned)(units8 * r.HV);
   constexpr unsigned block = C * 4;   // one wave per 16-row block
   if constexpr (PERCH) {
     if (dump) return launch(chunk_prep_kda_kernel<K, C, P, true>, grid, block, a, s);

@@ -134,14 +134,24 @@ __device__ __forceinline__ void store_half<f32x8>(f32x8* frag, int half, f32x4 v
   reinterpret_cast<f32x4*>(frag)[half] = v;
 }
 
-// XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin, so
-// give every slab of one unit (head or head segment) the same (id % 8) and
-// they share an L2.
-__device__ __forceinline__ bool unit_block(int nunits, int nslab, int& unit, int& sv) {
+// XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin.  A
+// group is one (batch, q/k head, segment); its G value heads and their slabs
+// get the same (id % 8) and consecutive slots, so every operand they share
+// (the q/k rows of the head, and each value head's W^ and A^ across its
+// slabs) is read through one L2.  unit = (batch * HV + value head) * nsegu
+// + segment.
+__device__ __forceinline__ bool unit_block(int B, int H, int G, int nsegu, int nslab, int& unit,
+                                           int& sv) {
   const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
-  unit = (slot / nslab) * 8 + xcd;
   sv = slot % nslab;
-  return unit < nunits;
+  const int gi = (slot / nslab) % G;
+  const long group = (long)(slot / nslab / G) * 8 + xcd;   // (b, h, segment)
+  if (group >= (long)B * H * nsegu) return false;
+  const int p = (int)(group % nsegu);
+  const long bhq = group / nsegu;
+  const long bh = (bhq / H) * (H * G) + (bhq % H) * G + gi;
+  unit = (int)(bh * nsegu + p);
+  return true;
 }
 
 // Offset (floats) of accumulator tile (state row tile dt, column tile ct) of
@@ -683,7 +693,7 @@ __global__ __launch_bounds__((scan_waves<K, C>() * 64)) void chunk_scan_kernel(S
 
   const int nsegu = FULL ? a.nseg : a.nseg - 1;       // segments handled by this pass
   int unit, sv;
-  if (!unit_block(a.B * a.HV * nsegu, NSLAB, unit, sv)) return;
+  if (!unit_block(a.B, a.H, a.HV / a.H, nsegu, NSLAB, unit, sv)) return;
   const int wv = wave_id();
   if constexpr (!FULL) {
     // in-place state: the first segment's first slab copies the head's

@@ -21,20 +21,23 @@ inline ScanArgs full_pass_args(const ScanArgs& a) {
 template <int K, int V, bool PERCH, class P, int BV, int C, bool LIN = false>
 gdr_status launch_scan_kvb(const Prob& r, ScanArgs& a, hipStream_t s) {
   constexpr int NW = scan_waves<K, C>();
-  const size_t BH = (size_t)r.B * r.HV;
-  auto grid_for = [](size_t units, int nslab) {
-    // units rounded up to a multiple of the 8 XCDs; surplus workgroups exit
-    return (unsigned)((units + 7) / 8 * 8 * nslab);
+  const size_t BHQ = (size_t)r.B * r.H;
+  const int G = r.HV / r.H;
+  auto grid_for = [&](int nsegu, int nslab) {
+    // (batch, q/k head, segment) groups rounded up to a multiple of the 8
+    // XCDs, times the value heads of a group and the slabs; surplus
+    // workgroups exit (see unit_block)
+    return (unsigned)((BHQ * nsegu + 7) / 8 * 8 * G * nslab);
   };
   gdr_status st;
   if (r.nseg > 1) {
     st = launch(chunk_scan_kernel<K, V, PERCH, P, kScanChain, BV, C, LIN>,
-                grid_for(BH * (r.nseg - 1), (K + V) / BV), NW * 64, a, s);
+                grid_for(r.nseg - 1, (K + V) / BV), NW * 64, a, s);
     if (st != GDR_OK) return st;
   }
   ScanArgs f = full_pass_args(a);
   return launch(chunk_scan_kernel<K, V, PERCH, P, kScanFull, BV, C, LIN>,
-                grid_for(BH * r.nseg, V / BV), NW * 64, f, s);
+                grid_for(r.nseg, V / BV), NW * 64, f, s);
 }
 
 // State columns per scan workgroup for 128-row chunks: 32 with K = 128 (8
