@@ -48,7 +48,7 @@ def test_noalloc_two_calls_match_chunk_fwd(gpu_lib):
 
 def test_noalloc_refuses_large_problem(gpu_lib):
     import torch
-    w = WORKLOADS[3].with_(T=2048)
+    w = WORKLOADS[3].with_(T=4096)
     prob = gpu_lib.problem(w.B, w.T, w.H, w.HV, w.K, w.V)
     assert gpu_lib.workspace_size(prob) > gpu_lib.NOALLOC_SCRATCH_BYTES
     inp = make_inputs(w)
