@@ -368,7 +368,8 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
 //        only the k-blocks kb <= I/2 of row tile I are stored, in order
 //        (ah_frag below), [C/16 (C/32 + 1) / 4 ... ][64][8]
 //   rs : 256 fp32: [0..C) exp(gamma_c) (one decay per row; 1 per channel),
-//        [C..C+K) exp(gamma_last) per key channel (C + K <= 256)
+//        [C..C+K) exp(gamma_last) per key channel in the state's row order
+//        (C + K <= 256); with one decay per row only [C] is written
 //   qh, kh : the scan's q and k operands as A fragments (rows c, k = d):
 //        [C/16][K/32][64][8] per chunk; lane (r, g) of fragment (ct, kb) holds
 //        key channels 32 kb + 8 g .. +7 of row 16 ct + r.  Per channel they

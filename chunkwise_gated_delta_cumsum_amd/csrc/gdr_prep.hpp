@@ -611,7 +611,8 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kernel(PrepArgs a) {
   {
     float* rs = a.rs + (size_t)cid * 256;
     for (int e = tid; e < C; e += NT) rs[e] = __expf(sGam[e]);
-    for (int e = tid; e < K; e += NT) rs[C + e] = __expf(sGam[C - 1]);
+    // one decay per row: exp(gamma_last) is one value for every key channel
+    if (tid == 0) rs[C] = __expf(sGam[C - 1]);
   }
   GDR_PPROF(7);
   GDR_PPROF_FLUSH;
