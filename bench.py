@@ -39,7 +39,9 @@ def traffic_model(w):
     stage (q, k, g, beta) and for the scan stage (q, k, v, o and the states).
     design: what each stage of this implementation is built to move, i.e.
     the compulsory bytes plus the workspace the prep kernel hands to the
-    scan kernel (and the per-channel q/k fragments).
+    scan kernel: W^, the compact A^, the row scalars and the fragment-order
+    q/k copies (per q/k head with one decay per row, per value head with
+    per-channel decay), which the scan reads in place of q and k.
     """
     C = w.chunk
     N = -(-w.T // C)
@@ -55,10 +57,11 @@ def traffic_model(w):
     state = w.B * w.HV * w.K * w.V * 4
     s0 = state if w.s0_std > 0 else 0
     ah_frags = (C // 16) * (C // 16 + 2) // 4        # lower-triangular A^ fragments
-    ws = nch * (C * w.K * wes + ah_frags * 512 * wes + 256 * 4)
-    qkh = 2 * nch * C * w.K * wes if w.per_channel else 0
+    rs = (C + (w.K if w.per_channel else 1)) * 4      # row scalars written and read
+    ws = nch * (C * w.K * wes + ah_frags * 512 * wes + rs)
+    qkh = 2 * (nch if w.per_channel else w.B * w.H * N) * C * w.K * wes
     design = dict(chunk_prep=qk + g + beta + ws + qkh,
-                  state_scan=(qkh if w.per_channel else qk) + v + ws + s0 + o + state)
+                  state_scan=qkh + v + ws + s0 + o + state)
     stage = dict(chunk_prep=qk + g + beta, state_scan=qk + v + o + s0 + state)
     compulsory = qk + v + g + beta + o + s0 + state
     return dict(design=design, stage=stage, compulsory=compulsory)
