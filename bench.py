@@ -89,15 +89,31 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(w, stage_kernels):
-    """HBM bytes per launch of a stage from the stored rocprofv3 FETCH_SIZE and
-    WRITE_SIZE counts (already scaled by the plain-copy calibration), or None
-    when there are none for this workload or the kernels changed since."""
+# the bench settings the stored counters were taken with (bench.py's defaults)
+COUNTER_SETTING = {"rule": "delta", "chunk": 64, "segments": 0, "slab": 0}
+
+
+def _counter_record(w, setting):
+    """The stored rocprofv3 counter record of a workload, or None when there is
+    none, the kernels changed since it was taken, or this run's settings
+    (rule, chunk length, forced segments or slab) differ from its own."""
     path = os.path.join(ROOT, "profiles", f"counters_{w.name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    if rec.get("setting", COUNTER_SETTING) != setting:
+        return None
+    return rec
+
+
+def measured_traffic(w, stage_kernels, setting=COUNTER_SETTING):
+    """HBM bytes per launch of a stage from the stored rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counts (already scaled by the plain-copy calibration), or None
+    (see _counter_record)."""
+    rec = _counter_record(w, setting)
+    if rec is None:
         return None
     total = 0.0
     found = False
@@ -108,15 +124,12 @@ def measured_traffic(w, stage_kernels):
     return total if found else None
 
 
-def measured_mfma(w):
+def measured_mfma(w, setting=COUNTER_SETTING):
     """MFMA busy fraction per kernel from the stored rocprofv3 counters
     (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x compute units), or None
-    when there are none for this workload or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", f"counters_{w.name}.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
-    if rec.get("sources_sha256") != kernel_sources_sha256():
+    (see _counter_record)."""
+    rec = _counter_record(w, setting)
+    if rec is None:
         return None
     out = {name: v["mfma_busy_frac"] for name, v in rec["kernels"].items()
            if "mfma_busy_frac" in v}
@@ -266,7 +279,8 @@ def bench_decode(args, w, inp):
                    "rotating_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w, ("decode_step_kernel",)),
+                     "traffic": measured_traffic(w, ("decode_step_kernel",), {
+                         **COUNTER_SETTING, "rule": args.rule, "slab": args.slab}),
                      "kernel": "decode_step", "kernels": ["decode_step_kernel"],
                      "algorithmic_bytes": nbytes, "kernel_ms": {"decode_step": kernel_ms}},
     }
@@ -438,7 +452,8 @@ def main():
     dom_ms, dom_kernels = stages[dom]
     dom_bytes = tm["stage"][dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w, dom_kernels)
+    setting = {"rule": args.rule, "chunk": w.chunk, "segments": args.segments, "slab": args.slab}
+    traffic = measured_traffic(w, dom_kernels, setting)
     nseg = gdr.scan_segments(prob)
     slab = gdr.scan_slab(prob)
     ms_per_step = elapsed / K * 1e3
@@ -483,7 +498,7 @@ def main():
                      "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak,
                      "design_bytes": tm["design"][dom],
                      "design_bytes_frac": tm["design"][dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "mfma_busy": measured_mfma(w)},
+                     "mfma_busy": measured_mfma(w, setting)},
         "fwd_entry_point_matches": same,
     }
     if not args.no_cpu_baseline:

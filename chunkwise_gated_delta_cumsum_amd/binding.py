@@ -98,7 +98,7 @@ def check(status: int) -> None:
         raise GdrError(status, status_string(status))
 
 
-def problem(B: int, T: int, H: int, HV: int, K: int, V: int, *, chunk: int = 64,
+def problem(B: int, T: int, H: int, HV: int, K: int, V: int, *, chunk: int = 0,
             per_channel: bool = False, scale: Optional[float] = None,
             dtype: str = "bf16", segments: int = 0, slab: int = 0,
             qk_l2norm: bool = False, rule: str = "delta",
@@ -217,7 +217,7 @@ def _check_state(name, t, B, HV, K, V):
         raise ValueError(f"{name} must be float32 [B, HV, K, V] = {(B, HV, K, V)}")
 
 
-def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
+def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 0,
                   scale: Optional[float] = None, *, output_final_state: bool = True,
                   workspace=None, out=None, segments: int = 0, slab: int = 0,
                   qk_l2norm: bool = False, rule: str = "delta", o_dtype: str = "fp32"
@@ -227,7 +227,7 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     q, k: [B, T, H, K]; v: [B, T, HV, V] (float32 or bfloat16, one dtype);
     g: [B, T, HV] or [B, T, HV, K] float32 log-decay; beta: [B, T, HV] float32;
     initial_state: [B, HV, K, V] float32 or None.  scale defaults to K**-0.5;
-    chunk is 64 or 128.
+    chunk is 64 or 128, or 0 for the automatic choice (64).
     Returns (o [B, T, HV, V], final_state [B, HV, K, V] float32 or None); o is
     float32, or bfloat16 with ``o_dtype="bf16"`` (the fp32 result rounded
     once, to nearest even).
@@ -272,7 +272,7 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     return o, s
 
 
-def gdr_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, chunk: int = 64,
+def gdr_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, chunk: int = 0,
                           scale: Optional[float] = None, *, output_final_state: bool = True,
                           out=None, segments: int = 0, slab: int = 0,
                           qk_l2norm: bool = False, rule: str = "delta", o_dtype: str = "fp32"
@@ -313,7 +313,7 @@ def gdr_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, chunk: int = 64,
     return o, s
 
 
-def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None, *,
+def gdr_chunk_prep(q, k, g, beta, chunk: int = 0, scale: Optional[float] = None, *,
                    V: Optional[int] = None, inspect: bool = False,
                    workspace=None, segments: int = 0, slab: int = 0,
                    qk_l2norm: bool = False, rule: str = "delta"
@@ -343,6 +343,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
     if inspect:
         B, T, H, K = q.shape
         HV = beta.shape[2]
+        chunk = chunk or 64               # the automatic chunk length
         N = -(-T // chunk)
         gshape = (B, HV, N, chunk, K) if prob.g_per_channel else (B, HV, N, chunk)
         ins = dict(gamma=torch.empty(gshape, dtype=torch.float32, device=dev),
@@ -357,7 +358,7 @@ def gdr_chunk_prep(q, k, g, beta, chunk: int = 64, scale: Optional[float] = None
     return workspace, ins
 
 
-def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 64,
+def gdr_chunk_scan(q, k, v, g, beta, workspace, initial_state=None, chunk: int = 0,
                    scale: Optional[float] = None, *, out=None, segments: int = 0,
                    slab: int = 0, qk_l2norm: bool = False, rule: str = "delta",
                    o_dtype: str = "fp32"):

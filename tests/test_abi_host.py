@@ -391,8 +391,17 @@ def test_chunk_128_problems(lib):
         assert gdr.scan_slab(base(T=1000, K=K, chunk=128, slab=bv)) == bv
         other = 64 if bv == 32 else 32
         assert name(call_fwd(lib, base(T=1000, K=K, chunk=128, slab=other))) == "GDR_ERR_UNSUPPORTED"
-    for C in (32, 96, 256, 0):
+    for C in (32, 96, 256):
         assert name(call_fwd(lib, base(chunk=C))) == "GDR_ERR_UNSUPPORTED"
+    assert name(call_fwd(lib, base(chunk=-64))) == "GDR_ERR_ARG"
+    # chunk 0 is the automatic choice: 64-row chunks, the same workspace,
+    # segments and slab as asking for 64
+    for kw in (dict(T=4096, H=12, HV=12), dict(T=16000, B=2, H=16, HV=32),
+               dict(T=8192, B=4, H=16, HV=16, per_channel=True), dict(T=300, K=64, V=64)):
+        auto, c64 = base(chunk=0, **kw), base(chunk=64, **kw)
+        assert gdr.workspace_size(auto) == gdr.workspace_size(c64) > 0
+        assert gdr.scan_segments(auto) == gdr.scan_segments(c64)
+        assert gdr.scan_slab(auto) == gdr.scan_slab(c64)
     # the workspace per token: the same W^ and q/k fragments, A^ keeps the
     # lower-triangular k-blocks (20 of 32 fragments at C = 128, 6 of 8 at 64)
     w64 = gdr.workspace_size(base(T=4096, H=12, HV=12, segments=1))

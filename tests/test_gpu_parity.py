@@ -215,6 +215,20 @@ def test_deterministic_and_stages_match(gpu_lib):
     assert np.array_equal(o3.cpu().numpy(), o1) and np.array_equal(s3.cpu().numpy(), s1)
 
 
+def test_auto_chunk_is_64(gpu_lib):
+    """chunk = 0 (the automatic choice) runs the 64-row kernels: bit-identical
+    results to asking for 64."""
+    import torch
+    for w in (WORKLOADS[3].with_(B=1, T=700), WORKLOADS[2].with_(B=1, T=300)):
+        inp = make_inputs(w)
+        t = to_device(inp)
+        args = (t["q"], t["k"], t["v"], t["g"], t["beta"], t["initial_state"])
+        o0, s0 = gpu_lib.gdr_chunk_fwd(*args, chunk=0, scale=inp.scale)
+        o64, s64 = gpu_lib.gdr_chunk_fwd(*args, chunk=64, scale=inp.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o64) and torch.equal(s0, s64)
+
+
 def test_state_in_place_and_optional(gpu_lib):
     import torch
     inp = make_inputs(WORKLOADS[3].with_(B=1, T=300))
