@@ -69,8 +69,8 @@ typedef enum gdr_status {
   GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query */
   GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
   GDR_ERR_HIP = 8,         /* a HIP query or kernel launch failed */
-  GDR_ERR_ARG = 9,         /* scale not finite, g_per_channel or qk_l2norm not 0/1,
-                              rule not a gdr_rule,
+  GDR_ERR_ARG = 9,         /* scale not finite, chunk < 0, g_per_channel or
+                              qk_l2norm not 0/1, rule not a gdr_rule,
                               scan_segments < 0, or scan_slab not 0, 32 or 64
                               (gdr_decode_step also takes 128) */
   GDR_ERR_ALIAS = 10,      /* an output overlaps an input or the other output
