@@ -359,6 +359,16 @@ __device__ __forceinline__ void store_ws4(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
+// A fragment's 8 elements to 8 consecutive workspace-type elements whose
+// address is 16-byte aligned (LDS or global)
+__device__ __forceinline__ void store_frag16(_Float16* p, half8 f) {
+  *reinterpret_cast<half8*>(p) = f;
+}
+__device__ __forceinline__ void store_frag16(float* p, f32x8 f) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
 // ---- workspace layout -----------------------------------------------------
 // Per chunk (one value head, C = 64 or 128 rows), in fragment order so every
 // lane reads or writes 8 consecutive elements:

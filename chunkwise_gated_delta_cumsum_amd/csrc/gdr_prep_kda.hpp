@@ -236,66 +236,135 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
     }
     for (int e = tid; e < C; e += NT) rs[e] = 1.f;
   }
+  lds_barrier();   // the tables are complete
 
   // ---- 2/3. own-block factors, earlier-row fragments, diagonal tiles ----------
-  // kl = k exp(s), ql = q exp(s): the later-row side (reference row 16I - 1);
-  // ke = k exp(s15 - s): the earlier-row side (reference row 16I + 15).
-  float kl[KB][8], ql[KB][8], ke[KB][8];
+  // kl = k exp(s), ql = q exp(s): the later-row side (reference row 16I - 1),
+  // kept as MFMA fragments for the off-diagonal tiles; ke = k exp(s15 - s):
+  // the earlier-row side (reference row 16I + 15), shared through LDS.  The
+  // same factors give this row's scan operands q exp(gamma) scale and
+  // k exp(gamma) (stored here) and its W^ operand row
+  // beta k exp(gamma_last - gamma) (kept as a fragment until its LDS tile is
+  // free), so no fp32 copy of the row outlives this loop.
+  frag_t kLf[KB], qLf[KB], wxf[KB];
   f32x4 dkk = zero4(), dqk = zero4();      // diagonal A_kk and A_qk^T tiles (raw dots)
   bool far = false;
+  const size_t off0 = (size_t)cid * NB * KB * 512 + ((size_t)I * KB) * 512 + lane * 8;
+  // Per k block in three parts, each of whose fp32 rows die at its end (the
+  // empty asm statements pin each fragment's conversion in place, and the
+  // scheduling fences keep the parts from overlapping): held together, the
+  // rows of every part would need more registers than three workgroups per
+  // CU leave.
+  auto qv_of = [&](int kb, int j) { return valid ? P::raw_f32(qr[kb], j) * fq : 0.f; };
+  auto kv_of = [&](int kb, int j) { return valid ? P::raw_f32(kr[kb], j) * fk : 0.f; };
+  auto f4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const f32x4 t15a = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 8 * grp);
-    const f32x4 t15b = *reinterpret_cast<const f32x4*>(sTot + I * K + 32 * kb + 8 * grp + 4);
-    const f32x4 tma = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 8 * grp);
-    const f32x4 tmb = *reinterpret_cast<const f32x4*>(sMid + I * K + 32 * kb + 8 * grp + 4);
-    float a1[8], b1[8], b2[8];
+    const int d0 = 32 * kb + 8 * grp;
+    {  // a. the later-row side and the scan operands
+      const f32x4 pa = f4(sPf + I * K + d0), pb = f4(sPf + I * K + d0 + 4);
+      float kl[8], ql[8], qx[8], kx[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float s15 = j < 4 ? t15a[j] : t15b[j - 4];
-      const float sm = j < 4 ? tma[j] : tmb[j - 4];
-      const float x = s[kb][j];
-      const float qv = valid ? P::raw_f32(qr[kb], j) * fq : 0.f;
-      const float kv = valid ? P::raw_f32(kr[kb], j) * fk : 0.f;
-      const float el = __expf(x);
-      kl[kb][j] = kv * el;
-      ql[kb][j] = qv * el;
-      ke[kb][j] = kv * __expf(s15 - x);
-      const float dl = x - sm;
-      far |= !(fabsf(dl) <= kDiagExpLimit);
-      const float dm = __expf(dl), dmi = __expf(-dl);
-      a1[j] = kv * dm;
-      b1[j] = kv * dmi;
-      b2[j] = qv * dm;
+      for (int j = 0; j < 8; ++j) {
+        const float el = __expf(s[kb][j]);
+        kl[j] = kv_of(kb, j) * el;
+        ql[j] = qv_of(kb, j) * el;
+        const float pf = j < 4 ? pa[j] : pb[j - 4];   // exp(gamma_i) = exp(s) exp(pre[I])
+        qx[j] = ql[j] * pf * a.scale;
+        kx[j] = kl[j] * pf;
+      }
+      kLf[kb] = P::make(kl);
+      qLf[kb] = P::make(ql);
+      asm volatile("" : "+v"(kLf[kb]), "+v"(qLf[kb]));
+      store_ws8(static_cast<ws_t*>(a.qh) + off0 + (size_t)kb * 512, qx);
+      store_ws8(static_cast<ws_t*>(a.kh) + off0 + (size_t)kb * 512, kx);
     }
-    if (I < NB - 1) sKE[(I * KB + kb) * 64 + lane] = P::make(ke[kb]);
-    const f32x8 fa1 = {a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]};
-    const f32x8 fb1 = {b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]};
-    const f32x8 fb2 = {b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]};
-    dkk = mma32(fa1, fb1, dkk);   // rows i, columns j of block I
-    dqk = mma32(fb1, fb2, dqk);   // rows c' (k), columns i (q) of block I
+    __builtin_amdgcn_sched_barrier(0);
+    {  // b. the earlier-row side and the W^ operand row
+      const f32x4 t15a = f4(sTot + I * K + d0), t15b = f4(sTot + I * K + d0 + 4);
+      const f32x4 wa = f4(sSf + I * K + d0), wb = f4(sSf + I * K + d0 + 4);
+      float ke[8], wx[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float s15 = j < 4 ? t15a[j] : t15b[j - 4];
+        ke[j] = kv_of(kb, j) * __expf(s15 - s[kb][j]);
+        // exp(gamma_last - gamma_i) = exp(s15 - s) exp(pre[NB] - pre[I+1])
+        wx[j] = bv * ke[j] * (j < 4 ? wa[j] : wb[j - 4]);
+      }
+      if (I < NB - 1) sKE[(I * KB + kb) * 64 + lane] = P::make(ke);
+      wxf[kb] = P::make(wx);
+      asm volatile("" : "+v"(wxf[kb]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {  // c. the diagonal tile, factored about the block's middle row
+      const f32x4 tma = f4(sMid + I * K + d0), tmb = f4(sMid + I * K + d0 + 4);
+      float a1[8], b1[8], b2[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float dl = s[kb][j] - (j < 4 ? tma[j] : tmb[j - 4]);
+        far |= !(fabsf(dl) <= kDiagExpLimit);
+        const float dm = __expf(dl), dmi = __expf(-dl);
+        const float kv = kv_of(kb, j);
+        a1[j] = kv * dm;
+        b1[j] = kv * dmi;
+        b2[j] = qv_of(kb, j) * dm;
+      }
+      const f32x8 fa1 = {a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]};
+      const f32x8 fb1 = {b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]};
+      const f32x8 fb2 = {b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]};
+      dkk = mma32(fa1, fb1, dkk);   // rows i, columns j of block I
+      dqk = mma32(fb1, fb2, dqk);   // rows c' (k), columns i (q) of block I
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (__any(far)) {
     // Explicit diagonal block: lane (r, grp) sums its channels for the pairs
     // (row r, row (r - m) mod 16), m = 0..15, the four channel groups are
     // added across lanes, and the entries are routed through LDS (the A_kk
-    // tile is not written yet) into accumulator layout.
+    // tile is not written yet) into accumulator layout.  This branch is rare:
+    // it loads its rows of g, q and k again (from L2) and redoes their
+    // cumsum, so that none of them has to stay live through the loop above.
+    raw_t qr2[KB], kr2[KB];
+    float s2[KB][8];
+    {
+      const int tt = min(t, T - 1);
+      const float* grow = a.g + (((size_t)b * T + tt) * a.HV + hv) * K;
+      const size_t qoff = (((size_t)b * T + tt) * a.H + h) * K;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 8 * grp);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(grow + 32 * kb + 8 * grp + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s2[kb][j] = row_scan16(valid ? g0[j] : 0.f);
+          s2[kb][4 + j] = row_scan16(valid ? g1[j] : 0.f);
+        }
+        qr2[kb] = P::load_raw8(static_cast<const in_t*>(a.q) + qoff + 32 * kb + 8 * grp);
+        kr2[kb] = P::load_raw8(static_cast<const in_t*>(a.k) + qoff + 32 * kb + 8 * grp);
+      }
+    }
     float* scr = sL + wave * 512;   // [2][16][16]
     for (int m = 0; m < 16; ++m) {
       const int jr = (r - m) & 15;
       const int src = jr + 16 * grp;
       float pk = 0.f, pq = 0.f;
+      // q and k are converted again in every pass from their 16-bit values
+      // (the empty asm keeps the fp32 rows from being held across the loop)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(qr2[kb]), "+v"(kr2[kb]));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float qv = valid ? P::raw_f32(qr[kb], j) * fq : 0.f;
-          const float kv = valid ? P::raw_f32(kr[kb], j) * fk : 0.f;
+          const float qv = valid ? P::raw_f32(qr2[kb], j) * fq : 0.f;
+          const float kv = valid ? P::raw_f32(kr2[kb], j) * fk : 0.f;
           const float kj = __shfl(kv, src, 64);
-          const float sj = __shfl(s[kb][j], src, 64);
-          const float e = __expf(s[kb][j] - sj);
+          const float sj = __shfl(s2[kb][j], src, 64);
+          const float e = __expf(s2[kb][j] - sj);
           pk += kv * kj * e;
           pq += qv * kj * e;
+          // a few exchanges in flight at a time, not all 64 of a pass
+          if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
       pk += __shfl_xor(pk, 16, 64);
       pk += __shfl_xor(pk, 32, 64);
@@ -329,7 +398,7 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
         }
     }
   }
-  lds_barrier();   // sKE and the tables are complete; the scratch is read
+  lds_barrier();   // sKE is complete; the diagonal scratch is read
   GDR_PPROF(2);
 
   // ---- off-diagonal tiles (J < I) ----------------------------------------------
@@ -337,12 +406,6 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) aqT[j] = zero4();
   if (I > 0) {
-    frag_t kLf[KB], qLf[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      kLf[kb] = P::make(kl[kb]);
-      qLf[kb] = P::make(ql[kb]);
-    }
     for (int J = 0; J < I; ++J) {
       const float* cf = sCf + (I * (I - 1) / 2 + J) * K;
       f32x4 akk = zero4(), aq = zero4();
@@ -375,38 +438,9 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
     aqT[I][j4] = rr <= cc ? dqk[j4] * sBeta[rr] * a.scale : 0.f;
   }
 
-  // ---- scan operands and the W^ operand ----------------------------------------
-  // (the W^ operand rows stay in registers until the tables are dead: their
-  // LDS tile takes the tables' bytes)
-  float wx[KB][8];
-  {
-    const size_t off0 = (size_t)cid * NB * KB * 512 + ((size_t)I * KB) * 512 + lane * 8;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int d0 = 32 * kb + 8 * grp;
-      const f32x4 pa = *reinterpret_cast<const f32x4*>(sPf + I * K + d0);
-      const f32x4 pb = *reinterpret_cast<const f32x4*>(sPf + I * K + d0 + 4);
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(sSf + I * K + d0);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(sSf + I * K + d0 + 4);
-      float qx[8], kx[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pf = j < 4 ? pa[j] : pb[j - 4];     // exp(gamma_i) = exp(s) exp(pre[I])
-        qx[j] = ql[kb][j] * pf * a.scale;
-        kx[j] = kl[kb][j] * pf;
-        // exp(gamma_last - gamma_i) = exp(s15 - s) exp(pre[NB] - pre[I+1])
-        wx[kb][j] = bv * ke[kb][j] * (j < 4 ? wa[j] : wb[j - 4]);
-      }
-      store_ws8(static_cast<ws_t*>(a.qh) + off0 + (size_t)kb * 512, qx);
-      store_ws8(static_cast<ws_t*>(a.kh) + off0 + (size_t)kb * 512, kx);
-    }
-  }
   lds_barrier();   // sL complete; sKE and the tables are dead
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    store_ws4(sSK + i * SP + 32 * kb + 8 * grp, wx[kb]);
-    store_ws4(sSK + i * SP + 32 * kb + 8 * grp + 4, wx[kb] + 4);
-  }
+  for (int kb = 0; kb < KB; ++kb) store_frag16(sSK + i * SP + 32 * kb + 8 * grp, wxf[kb]);
   lds_barrier();   // sSK complete
   GDR_PPROF(3);
 
