@@ -8,6 +8,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+# A host-side sanitizer build of the library to load instead of the product
+# one (set by tests/test_sanitizers.py for the child process it runs).
+if os.environ.get("GDR_TEST_LIBRARY"):
+    from chunkwise_gated_delta_cumsum_amd import binding as _binding
+    _binding.LIB_PATH = os.environ["GDR_TEST_LIBRARY"]
+
+
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
