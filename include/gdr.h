@@ -27,10 +27,12 @@
  *   final_state    [B, HV, K, V]   fp32 (output), or NULL to skip
  *
  * Ownership: the caller allocates and owns every buffer, the workspace
- * included.  The library never allocates or frees device memory; its only
- * global state is a per-device cache of the architecture check.  Calls on
+ * included.  The library never allocates or frees device memory; its global
+ * state is a per-device cache of the architecture check and, for
+ * gdr_chunk_fwd_noalloc only, a static device scratch array (one per GPU,
+ * held until the process ends) with its per-device address.  Calls on
  * different streams are independent when they use different workspaces and
- * outputs.
+ * outputs (gdr_chunk_fwd_noalloc calls on one GPU share its scratch array).
  *
  * Streams: work is enqueued asynchronously on `stream` (a hipStream_t; NULL
  * is the null stream).  No call synchronises.  A fault inside a kernel shows
@@ -42,7 +44,8 @@
  *
  * Numerics: with GDR_BF16 inputs the matrix products run on MFMA with fp16
  * operands and fp32 accumulation; the state, gamma, exponentials and o are
- * fp32 (o is rounded to bf16 only as it is stored, when o_dtype asks).  bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
+ * fp32 (o is rounded to bf16 only as it is stored, when o_dtype asks).
+ * bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
  * inputs every product runs in fp32.  With per-channel decay the decay is
  * folded into fp16 operands, which grow as exp(sum of the positive g of a
  * channel within one chunk): that sum must stay below about 8 (g <= 0, the
