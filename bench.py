@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--chunk", type=int, default=0, choices=(0, 64, 128),
+    ap.add_argument("--chunk", type=int, default=0, choices=(0, 32, 64, 128),
                     help="chunk length (0: the workload's, 64)")
     ap.add_argument("--segments", type=int, default=0,
                     help="sequence segments of the state scan (0: the library's choice)")

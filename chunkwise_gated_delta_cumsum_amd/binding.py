@@ -227,7 +227,7 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 0,
     q, k: [B, T, H, K]; v: [B, T, HV, V] (float32 or bfloat16, one dtype);
     g: [B, T, HV] or [B, T, HV, K] float32 log-decay; beta: [B, T, HV] float32;
     initial_state: [B, HV, K, V] float32 or None.  scale defaults to K**-0.5;
-    chunk is 64 or 128, or 0 for the automatic choice (64).
+    chunk is 32, 64 or 128, or 0 for the automatic choice (64).
     Returns (o [B, T, HV, V], final_state [B, HV, K, V] float32 or None); o is
     float32, or bfloat16 with ``o_dtype="bf16"`` (the fp32 result rounded
     once, to nearest even).

@@ -85,13 +85,15 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   if (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) return GDR_ERR_ARG;
   if (!std::isfinite(p->scale)) return GDR_ERR_ARG;
   if (p->chunk < 0) return GDR_ERR_ARG;
-  if (p->chunk != 0 && p->chunk != 64 && p->chunk != 128) return GDR_ERR_UNSUPPORTED;
+  if (p->chunk != 0 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128)
+    return GDR_ERR_UNSUPPORTED;
   if ((p->K != 64 && p->K != 128) || (p->V != 64 && p->V != 128)) return GDR_ERR_UNSUPPORTED;
   Prob r;
   r.B = p->B; r.T = p->T; r.H = p->H; r.HV = p->HV; r.K = p->K; r.V = p->V;
   // chunk 0: the automatic choice.  64-row chunks measured faster than
   // 128-row ones on every workload tried (the prep's C^2 work doubles per
-  // token while the scan's serial steps only halve), so it is 64.
+  // token while the scan's serial steps only halve) and than 32-row ones
+  // (twice the serial steps), so it is 64.
   r.C = p->chunk == 0 ? 64 : p->chunk;
   r.N = (p->T + r.C - 1) / r.C;
   r.perch = p->g_per_channel == 1;
@@ -213,6 +215,7 @@ gdr_status check_device() {
 
 gdr_status launch_scan(const Prob& r, ScanArgs& a, hipStream_t s) {
   if (r.C == 128) return r.f32 ? launch_scan128_f32(r, a, s) : launch_scan128_f16(r, a, s);
+  if (r.C == 32) return r.f32 ? launch_scan32_f32(r, a, s) : launch_scan32_f16(r, a, s);
   if (r.f32) return launch_scan_f32(r, a, s);
   if (r.linear && r.bv == 64) return launch_scan_f16_linear(r, a, s);
   return launch_scan_f16(r, a, s);

@@ -42,7 +42,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Chunk lengths the kernels are built for.  Every tiling works on 16-row
 // blocks of the chunk, one block per prep wave.
-constexpr int kChunkMin = 64, kChunkMax = 128;
+constexpr int kChunkMin = 32, kChunkMax = 128;
 
 // Barrier for LDS traffic only: wait for this wave's LDS operations, then
 // the workgroup barrier.  No kernel here reads global memory that another

@@ -39,11 +39,14 @@ inline gdr_status launch(Kern kern, unsigned grid, unsigned block, Args& args, h
 // Both stages and the decode step, on the caller's stream.
 gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s);
 gdr_status launch_prep128(const Prob& r, PrepArgs& a, bool dump, hipStream_t s);
+gdr_status launch_prep32(const Prob& r, PrepArgs& a, bool dump, hipStream_t s);
 gdr_status launch_scan_f16(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan_f16_linear(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan_f32(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan128_f16(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan128_f32(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_scan32_f16(const Prob& r, ScanArgs& a, hipStream_t s);
+gdr_status launch_scan32_f32(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_decode(int K, int V, int vb, bool perch, bool f32, DecodeArgs& a,
                          hipStream_t s);
 

@@ -1,6 +1,6 @@
 // Chunk preparation: everything that is parallel across chunks.
 //
-// One workgroup per (batch, value head, chunk of C = 64 or 128 rows), one
+// One workgroup per (batch, value head, chunk of C = 32, 64 or 128 rows), one
 // wave per 16-row block of the chunk (NB = C / 16 waves).  Steps, following
 // the sec-03 notes ("in-chunk cumsum and lower-triangular solve", "decayed
 // dot function") and the UT transform of the "Chunkwise parallel
@@ -454,14 +454,16 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qr[kb] = P::load_raw8(qp + 32 * kb);
   }
-  constexpr int GPL = C / 64;     // g, beta values per lane of wave 0
+  // g, beta values per lane of wave 0 (lanes past C hold zeros: with 32-row
+  // chunks half the wave)
+  constexpr int GPL = (C + 63) / 64;
   float gv[GPL], bv[GPL];
   if (wave == 0) {
 #pragma unroll
     for (int u = 0; u < GPL; ++u) {
       const int t = t0 + 64 * u + lane;
       gv[u] = bv[u] = 0.f;
-      if (t < T) {
+      if (64 * u + lane < C && t < T) {
         const size_t idx = ((size_t)b * T + t) * a.HV + hv;
         gv[u] = a.g[idx];
         bv[u] = a.beta[idx];
@@ -531,9 +533,11 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kernel(PrepArgs a) {
     // base is now gamma_last
 #pragma unroll
     for (int u = 0; u < GPL; ++u) {
-      sGam[64 * u + lane] = gv[u];
-      sBeta[64 * u + lane] = bv[u];
-      sKs[64 * u + lane] = bv[u] * __expf(base - gv[u]);
+      if (64 * u + lane < C) {
+        sGam[64 * u + lane] = gv[u];
+        sBeta[64 * u + lane] = bv[u];
+        sKs[64 * u + lane] = bv[u] * __expf(base - gv[u]);
+      }
     }
   }
   lds_barrier();

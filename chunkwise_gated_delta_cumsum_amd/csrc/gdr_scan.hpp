@@ -106,9 +106,9 @@ constexpr int kScanChain = 1;
 
 // Waves per scan workgroup: one 16-row tile of the chunk and K/16/NW state
 // row tiles each; 128-row chunks with K = 128 take 8 waves (one chunk row
-// tile and one state row tile each), everything else 4.
+// tile and one state row tile each), 32-row chunks 2, everything else 4.
 template <int K, int C>
-constexpr int scan_waves() { return (C == 128 && K == 128) ? 8 : 4; }
+constexpr int scan_waves() { return C == 32 ? 2 : (C == 128 && K == 128) ? 8 : 4; }
 
 
 // Calls f(std::integral_constant<int, I>{}) for I = B .. E-1.

@@ -48,10 +48,14 @@ constexpr int slab_c128() { return K == 128 ? 32 : 64; }
 
 // LINEAR selects the linear rule's instantiation (64-column slabs, 64-row
 // chunks); otherwise the general kernels at the problem's slab width.
+// 32-row chunks take the general kernels (2 waves) at 32 or 64 columns.
 template <int K, int V, bool PERCH, class P, bool LINEAR, int C>
 gdr_status launch_scan_kv(const Prob& r, ScanArgs& a, hipStream_t s) {
   if constexpr (C == 128) {
     return launch_scan_kvb<K, V, PERCH, P, slab_c128<K>(), 128>(r, a, s);
+  } else if constexpr (C == 32) {
+    return r.bv == 32 ? launch_scan_kvb<K, V, PERCH, P, 32, 32>(r, a, s)
+                      : launch_scan_kvb<K, V, PERCH, P, 64, 32>(r, a, s);
   } else if constexpr (LINEAR) {
     return launch_scan_kvb<K, V, PERCH, P, 64, 64, true>(r, a, s);
   } else {

@@ -66,8 +66,8 @@ typedef enum gdr_status {
   GDR_ERR_NULL = 1,        /* a required pointer (problem, q, k, v, g, beta, o) is NULL */
   GDR_ERR_SHAPE = 2,       /* B, T, H, HV, K or V < 1, or HV % H != 0 */
   GDR_ERR_DTYPE = 3,       /* qkv_dtype or o_dtype is not a gdr_dtype value */
-  GDR_ERR_UNSUPPORTED = 4, /* valid but not built: chunk not 0, 64 or 128, K or V not
-                              64 or 128, or a scan_slab the chunk length lacks */
+  GDR_ERR_UNSUPPORTED = 4, /* valid but not built: chunk not 0, 32, 64 or 128, K or V
+                              not 64 or 128, or a scan_slab the chunk length lacks */
   GDR_ERR_ALIGN = 5,       /* a tensor or workspace pointer is not 16-byte aligned */
   GDR_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query */
   GDR_ERR_DEVICE = 7,      /* the current HIP device is not a gfx950 */
@@ -101,9 +101,10 @@ typedef enum gdr_rule { GDR_RULE_DELTA = 0, GDR_RULE_LINEAR = 1 } gdr_rule;
 
 typedef struct gdr_problem {
   int32_t B, T, H, HV, K, V; /* batch, tokens, q/k heads, value heads, key dim, value dim */
-  int32_t chunk;             /* chunk length C: 64 or 128, or 0 for the automatic
-                                choice, which is 64 (faster than 128 on every
-                                workload measured); negative: GDR_ERR_ARG */
+  int32_t chunk;             /* chunk length C: 32, 64 or 128, or 0 for the
+                                automatic choice, which is 64 (faster than 32
+                                and 128 on every workload measured);
+                                negative: GDR_ERR_ARG */
   int32_t g_per_channel;     /* 0: g[B,T,HV]; 1: g[B,T,HV,K] */
   float scale;               /* query scale; callers usually pass 1/sqrt(K) */
   int32_t qkv_dtype;         /* gdr_dtype of q, k and v */

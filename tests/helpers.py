@@ -19,6 +19,21 @@ def rel_err(x, ref) -> float:
     return float(np.abs(x - ref).max() / rms)
 
 
+def rel_err_rows(o, s, ro, rs):
+    """The same metric taken row by row: the final state per (batch, value
+    head, key channel) row and o per token, each against the rms of its own
+    reference row (the worst row is returned for each).  For decays above 1
+    per key channel the state's channel rows grow at different rates, as the
+    exp of each channel's own decay sum, so their magnitudes spread over
+    orders and max|delta| / rms over the whole tensor compares the error of
+    the largest rows with the rms of all; per row, every value is compared
+    with values of its own scale."""
+    o, s, ro, rs = (np.asarray(x, dtype=np.float64) for x in (o, s, ro, rs))
+    ds = np.abs(s - rs).max(axis=-1) / np.sqrt((rs ** 2).mean(axis=-1))
+    do = np.abs(o - ro).max(axis=(0, 2, 3)) / np.sqrt((ro ** 2).mean(axis=(0, 2, 3)))
+    return float(do.max()), float(ds.max())
+
+
 def to_device(inp, device="cuda"):
     """torch tensors on `device` holding exactly the generated values."""
     import torch

@@ -7,11 +7,14 @@
 namespace gdr {
 gdr_status launch_prep(const Prob&, PrepArgs&, bool, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_prep128(const Prob&, PrepArgs&, bool, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_prep32(const Prob&, PrepArgs&, bool, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan_f16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan_f16_linear(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan_f32(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan128_f16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan128_f32(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_scan32_f16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_scan32_f32(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_decode(int, int, int, bool, bool, DecodeArgs&, hipStream_t) {
   return GDR_ERR_HIP;
 }

@@ -96,7 +96,7 @@ def test_workspace_size(lib):
     (dict(H=3, HV=4), "GDR_ERR_SHAPE"),
     (dict(K=96), "GDR_ERR_UNSUPPORTED"),
     (dict(V=256), "GDR_ERR_UNSUPPORTED"),
-    (dict(chunk=32), "GDR_ERR_UNSUPPORTED"),
+    (dict(chunk=48), "GDR_ERR_UNSUPPORTED"),
     (dict(scale=float("nan")), "GDR_ERR_ARG"),
     (dict(scale=float("inf")), "GDR_ERR_ARG"),
 ])
@@ -380,9 +380,9 @@ def test_noalloc_validation(lib):
     assert gdr.workspace_size(base(T=4096, H=12, HV=12)) <= binding.NOALLOC_SCRATCH_BYTES
 
 
-def test_chunk_128_problems(lib):
-    """Chunk lengths 64 and 128 are built; 128-row chunks use one slab width
-    per key dimension (32 columns for K = 128, 64 for K = 64)."""
+def test_chunk_length_problems(lib):
+    """Chunk lengths 32, 64 and 128 are built; 128-row chunks use one slab
+    width per key dimension (32 columns for K = 128, 64 for K = 64)."""
     name = lambda st: binding.STATUS_NAMES[st]
     for K, bv in ((128, 32), (64, 64)):
         p = base(T=1000, K=K, V=128, chunk=128)
@@ -391,8 +391,15 @@ def test_chunk_128_problems(lib):
         assert gdr.scan_slab(base(T=1000, K=K, chunk=128, slab=bv)) == bv
         other = 64 if bv == 32 else 32
         assert name(call_fwd(lib, base(T=1000, K=K, chunk=128, slab=other))) == "GDR_ERR_UNSUPPORTED"
-    for C in (32, 96, 256):
+    for C in (16, 48, 96, 256):
         assert name(call_fwd(lib, base(chunk=C))) == "GDR_ERR_UNSUPPORTED"
+    # 32-row chunks: the general kernels at 32 or 64 columns (64 by default)
+    for K in (64, 128):
+        p = base(T=1000, K=K, V=128, chunk=32)
+        assert gdr.workspace_size(p) > 0
+        assert gdr.scan_slab(p) == 64
+        for bv in (32, 64):
+            assert gdr.scan_slab(base(T=1000, K=K, chunk=32, slab=bv)) == bv
     assert name(call_fwd(lib, base(chunk=-64))) == "GDR_ERR_ARG"
     # chunk 0 is the automatic choice: 64-row chunks, the same workspace,
     # segments and slab as asking for 64

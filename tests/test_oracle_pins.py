@@ -55,7 +55,7 @@ def test_golden_hand_derived(path):
 
 # ------------------------------------------- chunk form == recurrence -------
 @pytest.mark.parametrize("per_channel", [False, True])
-@pytest.mark.parametrize("C", [1, 16, 64, 128, 200])
+@pytest.mark.parametrize("C", [1, 16, 32, 64, 128, 200])
 @pytest.mark.parametrize("T,H,HV,s0", [(200, 2, 2, False), (130, 1, 2, True),
                                        (77, 2, 4, True)])
 def test_chunk_form_equals_recurrence(per_channel, C, T, H, HV, s0):
