@@ -411,6 +411,9 @@ def main():
     torch.cuda.synchronize()
     step_prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     step_scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    # per-step durations of that run (events on the launch stream), for the
+    # median and fastest step beside the timed mean
+    step_each = sorted(e[0].elapsed_time(e[2]) for e in evs)
 
     # Per-stage launch durations: each stage alone, launched back to back over
     # the rotating sets between one pair of events on the launch stream (the
@@ -500,6 +503,13 @@ def main():
                      "design_bytes_frac": tm["design"][dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "mfma_busy": measured_mfma(w, setting)},
         "fwd_entry_point_matches": same,
+        # the same steps one by one with events around each (a separate,
+        # untimed run): median and fastest step, and the tokens/s and path
+        # fraction of the median step
+        "step_events": {"median_ms": step_each[len(step_each) // 2], "min_ms": step_each[0],
+                        "tokens_per_s_median": tokens / (step_each[len(step_each) // 2] * 1e-3),
+                        "path_hbm_frac_median": tm["compulsory"] / (
+                            step_each[len(step_each) // 2] * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule,
