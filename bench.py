@@ -290,15 +290,24 @@ def bench_decode(args, w, inp):
 
 
 def copy_calibration(mib, reps):
-    """Plain device copy of known size, for scaling rocprof FETCH/WRITE_SIZE."""
+    """Plain device copy of known size, for scaling rocprof FETCH/WRITE_SIZE;
+    also reports the copy's own rate (bytes read plus written per second), the
+    HBM rate a plain streaming kernel reaches on this GPU."""
     import torch
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"calibration_copy_bytes": n * 4, "reps": reps}), flush=True)
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"calibration_copy_bytes": n * 4, "reps": reps, "ms_per_copy": ms,
+                      "copy_GBps": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def main():
