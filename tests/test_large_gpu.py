@@ -23,7 +23,7 @@ from helpers import TOL, rel_err
 
 pytestmark = pytest.mark.gpu
 
-T = (1 << 20) + 37     # 16385 chunks, ragged tail
+T = (1 << 20) + 37     # a ragged tail at every chunk length (16385 chunks of 64)
 H = HV = 17            # T * H * K = 2.28e9 elements > 2^31
 K = V = 128
 W = 256                # active tokens at the end
@@ -39,10 +39,12 @@ def _samples():
     return np.array(sorted(s))
 
 
-@pytest.mark.parametrize("per_channel", [False, True], ids=["scalar_g", "per_channel_g"])
-def test_max_size_offsets(gpu_lib, per_channel):
+@pytest.mark.parametrize("per_channel,chunk", [(False, 64), (True, 64), (False, 32), (True, 128)],
+                         ids=["scalar_g", "per_channel_g", "scalar_g_C32", "per_channel_g_C128"])
+def test_max_size_offsets(gpu_lib, per_channel, chunk):
     import torch
-    print(f"max-size case: B=1 T={T} H=HV={H} K=V={K} per_channel={per_channel}", flush=True)
+    print(f"max-size case: B=1 T={T} H=HV={H} K=V={K} per_channel={per_channel} C={chunk}",
+          flush=True)
     dev = "cuda"
     gen = torch.Generator(device=dev)
     gen.manual_seed(91 + int(per_channel))
@@ -67,10 +69,10 @@ def test_max_size_offsets(gpu_lib, per_channel):
     s0 = 0.1 * torch.randn(1, HV, K, V, generator=gen, device=dev)
     scale = K ** -0.5
 
-    prob = gpu_lib.problem(1, T, H, HV, K, V, per_channel=per_channel, scale=scale)
+    prob = gpu_lib.problem(1, T, H, HV, K, V, per_channel=per_channel, scale=scale, chunk=chunk)
     print(f"scan segments: {gpu_lib.scan_segments(prob)}, workspace "
           f"{gpu_lib.workspace_size(prob) / 2**30:.1f} GiB", flush=True)
-    o, s = gpu_lib.gdr_chunk_fwd(q, k, v, g, beta, s0, chunk=64, scale=scale)
+    o, s = gpu_lib.gdr_chunk_fwd(q, k, v, g, beta, s0, chunk=chunk, scale=scale)
     torch.cuda.synchronize()
 
     def host(x):
