@@ -113,9 +113,11 @@ typedef struct gdr_problem {
                                 asks for n (rounded so that every segment holds
                                 the same number of chunks, at most one per chunk) */
   int32_t scan_slab;         /* state columns per state-scan workgroup: 0 chooses
-                                automatically (gdr_chunk_scan_slab), or 32 or 64;
-                                any width gives the same result up to rounding
-                                order, it only moves work between workgroups */
+                                automatically (gdr_chunk_scan_slab), or 32 or 64
+                                (with 128-row chunks only 32 for K = 128 and 64
+                                for K = 64 are built); any width gives the same
+                                result up to rounding order, it only moves work
+                                between workgroups */
   int32_t qk_l2norm;         /* 1: L2-normalise every q and k row inside the
                                 kernels first, x * rsqrt(sum(x^2) + 1e-6) (the
                                 scalar-g kernel page's optional normaliser);
