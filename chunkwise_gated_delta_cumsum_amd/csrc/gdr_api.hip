@@ -198,18 +198,18 @@ bool out_overlaps(Span out, std::initializer_list<Span> ins) {
 }
 
 gdr_status check_device() {
-  static std::atomic<int> verdict[64];  // 0 unknown, 1 gfx950, 2 other (per device ordinal)
+  static std::atomic<int> arch_state[64];  // 0 unknown, 1 gfx950, 2 other (per device ordinal)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_HIP;
   if (dev >= 0 && dev < 64) {
-    const int v = verdict[dev].load(std::memory_order_relaxed);
+    const int v = arch_state[dev].load(std::memory_order_relaxed);
     if (v == 1) return GDR_OK;
     if (v == 2) return GDR_ERR_DEVICE;
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GDR_ERR_HIP;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev >= 0 && dev < 64) verdict[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (dev >= 0 && dev < 64) arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? GDR_OK : GDR_ERR_DEVICE;
 }
 
