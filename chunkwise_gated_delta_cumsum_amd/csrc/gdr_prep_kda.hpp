@@ -20,9 +20,10 @@
 //      fp16 range.  The first factor goes on the later row (register
 //      fragments of block I), the other two on the earlier row (block J's
 //      fragment, shared through LDS, times a per-channel table).
-//   3. Diagonal tiles factor about the block's middle row m in fp32,
-//      exp(s_i - s_m) exp(s_m - s_j), on fp32 MFMA; exact while |s - s_m| <=
-//      80 on the block.  Beyond that (decays near e^-80 within 8 rows) the
+//   3. Diagonal tiles factor about the block's middle row m,
+//      exp(s_i - s_m) exp(s_m - s_j): with fp16 operands while |s - s_m| <= 4
+//      on the block (16-bit inputs), else on fp32 MFMA, exact while
+//      |s - s_m| <= 80.  Beyond that (decays near e^-80 within 8 rows) the
 //      wave sums the 16x16 entries explicitly, exp per channel and entry.
 //   4. q exp(gamma) scale and k exp(gamma) (the scan's operands) and
 //      beta k exp(gamma_last - gamma) (for W^) from the same factors and the
@@ -37,6 +38,11 @@ namespace gdr {
 
 // Threshold of the fp32 middle-row factorisation of a diagonal block.
 constexpr float kDiagExpLimit = 80.f;
+// Within e^+-4 of the middle row every factor of a diagonal block's operands
+// is in the fp16 normal range for rows of unit scale (|x| e^4 < 65504, and
+// the entries of the strictly lower part carry e^(s_i - s_j) <= 1 for
+// g <= 0), so the 16-bit path forms the diagonal tiles with fp16 operands.
+constexpr float kDiagF16Limit = 4.f;
 
 // Inclusive scan across the 16 lanes of each DPP row (lanes 16g .. 16g+15).
 template <int N>
@@ -299,21 +305,31 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
     {  // c. the diagonal tile, factored about the block's middle row
       const f32x4 tma = f4(sMid + I * K + d0), tmb = f4(sMid + I * K + d0 + 4);
       float a1[8], b1[8], b2[8];
+      bool wide = false;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float dl = s[kb][j] - (j < 4 ? tma[j] : tmb[j - 4]);
         far |= !(fabsf(dl) <= kDiagExpLimit);
+        wide |= !(fabsf(dl) <= kDiagF16Limit);
         const float dm = __expf(dl), dmi = __expf(-dl);
         const float kv = kv_of(kb, j);
         a1[j] = kv * dm;
         b1[j] = kv * dmi;
         b2[j] = qv_of(kb, j) * dm;
       }
-      const f32x8 fa1 = {a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]};
-      const f32x8 fb1 = {b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]};
-      const f32x8 fb2 = {b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]};
-      dkk = mma32(fa1, fb1, dkk);   // rows i, columns j of block I
-      dqk = mma32(fb1, fb2, dqk);   // rows c' (k), columns i (q) of block I
+      if (P::kF32 || __any(wide)) {
+        const f32x8 fa1 = {a1[0], a1[1], a1[2], a1[3], a1[4], a1[5], a1[6], a1[7]};
+        const f32x8 fb1 = {b1[0], b1[1], b1[2], b1[3], b1[4], b1[5], b1[6], b1[7]};
+        const f32x8 fb2 = {b2[0], b2[1], b2[2], b2[3], b2[4], b2[5], b2[6], b2[7]};
+        dkk = mma32(fa1, fb1, dkk);   // rows i, columns j of block I
+        dqk = mma32(fb1, fb2, dqk);   // rows c' (k), columns i (q) of block I
+      } else {
+        // every factor within e^+-kDiagF16Limit: fp16 operands, the
+        // precision of the off-diagonal tiles, in one MFMA instead of eight
+        const frag_t ha1 = P::make(a1), hb1 = P::make(b1), hb2 = P::make(b2);
+        dkk = mma32(ha1, hb1, dkk);
+        dqk = mma32(hb1, hb2, dqk);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
