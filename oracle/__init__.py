@@ -39,6 +39,13 @@ Pins (tests/test_oracle_pins.py, CPU only), one or more per function:
                           row iteration agree (three forms the pages give).
 * ``l2norm_rows``      -- a hand-derived row, the closed-form norm of any
                           output row, the kept direction and the zero row.
+
+Property tests (tests/test_properties.py, Hypothesis on tiny shapes) add,
+for ``recurrence``, ``chunk_forward`` and the ``ut_inverse_*`` forms: the
+chunk form at any chunk length, the Kronecker form of both rules, key and
+value channel relabelling, a cut anywhere with the state carried, batch
+independence, linearity in the scale, the closed form at beta = 0, the
+linear rule's quadratic form, and the inverses' agreement on any size.
 """
 from .recurrence import build, num_threads, recurrence, recurrence_heads  # noqa: F401
 from .chunk_form import (chunk_forward, decayed_dot, ut_inverse_neumann,  # noqa: F401
