@@ -28,10 +28,12 @@ STATUS_NAMES = {
     11: "GDR_ERR_SCRATCH",
 }
 NOALLOC_SCRATCH_BYTES = 64 << 20    # GDR_NOALLOC_SCRATCH_BYTES in gdr.h
+# gdr_check_bit: the bits gdr_check_inputs sets
+CHECK_BITS = {1: "GDR_CHECK_NONFINITE", 2: "GDR_CHECK_FP16_RANGE", 4: "GDR_CHECK_DECAY_RANGE"}
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc",
             "gdr_chunk_prep",
             "gdr_chunk_scan", "gdr_chunk_scan_segments", "gdr_chunk_scan_slab",
-            "gdr_decode_step", "gdr_status_string", "gdr_version")
+            "gdr_decode_step", "gdr_check_inputs", "gdr_status_string", "gdr_version")
 
 
 class GdrProblem(ctypes.Structure):
@@ -83,6 +85,8 @@ def load():
     lib.gdr_decode_step.argtypes = [P] + [vp] * 8 + [vp]
     lib.gdr_decode_step.restype = ctypes.c_int
     lib.gdr_chunk_scan_slab.restype = ctypes.c_int
+    lib.gdr_check_inputs.argtypes = [P] + [vp] * 6 + [vp]
+    lib.gdr_check_inputs.restype = ctypes.c_int
     lib.gdr_version.argtypes = []
     lib.gdr_version.restype = ctypes.c_int
     _lib = lib
@@ -270,6 +274,37 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 0,
                            _nbytes(workspace), _stream(dev))
     check(st)
     return o, s
+
+
+def gdr_check_inputs(q, k, v, g, beta, chunk: int = 0, *, qk_l2norm: bool = False,
+                     flags=None) -> "torch.Tensor":
+    """Checks the forward pass's inputs against its numeric preconditions on
+    the device (gdr_check_inputs in gdr.h).  Returns the one-element int32
+    device tensor (``flags`` if given) that the library sets, on torch's
+    current stream, to the OR of the violated CHECK_BITS (0: none); reading it
+    synchronises.  ``chunk`` and ``qk_l2norm`` are those of the forward call
+    the inputs are meant for."""
+    import torch
+    lib = load()
+    dev = q.device
+    _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta)
+    prob = _problem_from(q, k, v, g, beta, chunk, None, qk_l2norm=qk_l2norm)
+    if flags is None:
+        _require_gpu(dev)
+        flags = torch.empty(1, dtype=torch.int32, device=dev)
+    elif flags.dtype != torch.int32 or flags.numel() < 1:
+        raise TypeError("flags must be an int32 tensor of at least one element")
+    else:
+        _check_tensors(dev, flags=flags)
+        _require_gpu(dev)
+    check(lib.gdr_check_inputs(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(flags), _stream(dev)))
+    return flags
+
+
+def check_bit_names(bits: int) -> list:
+    """Names of the CHECK_BITS set in ``bits``."""
+    return [name for bit, name in CHECK_BITS.items() if bits & bit]
 
 
 def gdr_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, chunk: int = 0,

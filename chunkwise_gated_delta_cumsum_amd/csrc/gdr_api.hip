@@ -385,6 +385,36 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   return launch_decode(p->K, p->V, vb, p->g_per_channel == 1, f32, a, hs);
 }
 
+gdr_status gdr_check_inputs(const gdr_problem* p, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, uint32_t* flags,
+                            void* stream) {
+  Prob r;
+  gdr_status st = validate(p, &r);
+  if (st != GDR_OK) return st;
+  if (!q || !k || !v || !g || !beta || !flags) return GDR_ERR_NULL;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)g,
+                          (const void*)beta})
+    if (!aligned16(ptr)) return GDR_ERR_ALIGN;
+  if (((uintptr_t)flags & 3u) != 0) return GDR_ERR_ALIGN;
+  const Spans sp = spans(r, q, k, v, g, beta, nullptr, nullptr, nullptr, nullptr, 0);
+  if (out_overlaps({flags, sizeof(uint32_t)}, {sp.q, sp.k, sp.v, sp.g, sp.beta}))
+    return GDR_ERR_ALIAS;
+  st = check_device();
+  if (st != GDR_OK) return st;
+  CheckArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.flags = flags;
+  const size_t tok = (size_t)r.B * r.T;
+  a.nqk = tok * r.H * r.K;
+  a.nv = tok * r.HV * r.V;
+  a.nbeta = tok * r.HV;
+  a.B = r.B; a.T = r.T; a.HV = r.HV; a.K = r.K; a.C = r.C; a.N = r.N;
+  a.perch = r.perch;
+  a.bf16 = !r.f32;
+  a.qk_range = !r.f32 && !r.l2norm;
+  a.decay = !r.f32;
+  return launch_check(r, a, static_cast<hipStream_t>(stream));
+}
+
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
   Prob r;
   if (validate(p, &r) != GDR_OK) return 0;
@@ -515,6 +545,6 @@ int gdr_chunk_scan_slab(const gdr_problem* p) {
   return r.bv;
 }
 
-int gdr_version(void) { return 300; }   // 0.3.0: gdr_problem gained o_dtype
+int gdr_version(void) { return 400; }   // 0.4.0: gdr_check_inputs added
 
 }  // extern "C"

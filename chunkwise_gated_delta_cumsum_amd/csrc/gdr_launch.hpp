@@ -2,12 +2,14 @@
 // the C ABI) and the launcher translation units, one per kernel family
 // (gdr_launch_prep.hip, gdr_launch_prep128.hip, gdr_launch_scan_f16.hip,
 // gdr_launch_scan_lin.hip, gdr_launch_scan_f32.hip, gdr_launch_scan128_f16.hip,
-// gdr_launch_scan128_f32.hip, gdr_launch_decode.hip), which instantiate the
+// gdr_launch_scan128_f32.hip, gdr_launch_scan32_f16.hip, gdr_launch_scan32_f32.hip,
+// gdr_launch_prep32.hip, gdr_launch_decode.hip, gdr_launch_check.hip), which instantiate the
 // kernels and compile in parallel.
 #pragma once
 #include <hip/hip_runtime.h>
 
 #include "gdr.h"
+#include "gdr_check.hpp"
 #include "gdr_decode.hpp"
 #include "gdr_prep_kda.hpp"
 #include "gdr_scan.hpp"
@@ -49,5 +51,7 @@ gdr_status launch_scan32_f16(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_scan32_f32(const Prob& r, ScanArgs& a, hipStream_t s);
 gdr_status launch_decode(int K, int V, int vb, bool perch, bool f32, DecodeArgs& a,
                          hipStream_t s);
+// The input range check (clears a.flags, then one pass over the inputs).
+gdr_status launch_check(const Prob& r, CheckArgs& a, hipStream_t s);
 
 }  // namespace gdr

@@ -46,10 +46,13 @@
  * operands and fp32 accumulation; the state, gamma, exponentials and o are
  * fp32 (o is rounded to bf16 only as it is stored, when o_dtype asks).
  * bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
- * inputs every product runs in fp32.  With per-channel decay the decay is
- * folded into fp16 operands, which grow as exp(sum of the positive g of a
- * channel within one chunk): that sum must stay below about 8 (g <= 0, the
- * usual log-decay, is always in range).
+ * inputs every product runs in fp32.  With bf16 inputs the decay is folded
+ * into fp16 operands, which grow as exp(sum of the positive g of a channel,
+ * or of the row decay, within one chunk): that sum must stay at or below 8
+ * (g <= 0, the usual log-decay, is always in range).  The state enters its
+ * products as fp16 too, so its entries must stay below 65504 in magnitude.
+ * gdr_check_inputs tests the inputs against these bounds on the device;
+ * nothing else checks them, and a violation shows as inf or NaN in o.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -238,6 +241,34 @@ gdr_status gdr_decode_step(const gdr_problem* p,
                            const float* g, const float* beta,
                            const float* state_in, float* state_out, void* o,
                            void* stream);
+
+/* Bits of the word gdr_check_inputs writes. */
+typedef enum gdr_check_bit {
+  GDR_CHECK_NONFINITE = 1,   /* a NaN or an infinity in q, k, v, g or beta */
+  GDR_CHECK_FP16_RANGE = 2,  /* bf16 q, k or v with |x| >= 65520, which rounds to
+                                infinity in fp16 (q and k are exempt with
+                                qk_l2norm = 1: they are scaled in fp32 first) */
+  GDR_CHECK_DECAY_RANGE = 4  /* bf16 inputs: within some chunk of the problem's
+                                chunk length, the positive g of one channel (or
+                                of the row decay) sum to more than 8 */
+} gdr_check_bit;
+
+/* Checks the inputs of gdr_chunk_fwd (or of the stage calls) for problem `p`
+ * against the numeric preconditions of the numerics notes above, on the
+ * device: one pass over q, k, v, g and beta, which are only read.  Sets
+ * *flags (device memory, 4-byte aligned, not overlapping any input) to the
+ * OR of the gdr_check_bit values of every violation found, 0 when there is
+ * none; the word is written on `stream`, so read it after synchronising.
+ * With GDR_F32 inputs only GDR_CHECK_NONFINITE can be set (every product is
+ * fp32).  Validation (GDR_ERR_NULL, _SHAPE, _DTYPE, _ARG, _UNSUPPORTED,
+ * _ALIGN, _ALIAS, _DEVICE) as for gdr_chunk_fwd; the state's own range
+ * (see above) depends on the whole recurrence and is not checked.  The
+ * pass is bound by HBM bandwidth on the inputs' bytes: an optional
+ * validation step, not part of the forward pass. */
+gdr_status gdr_check_inputs(const gdr_problem* p,
+                            const void* q, const void* k, const void* v,
+                            const float* g, const float* beta,
+                            uint32_t* flags, void* stream);
 
 /* Number of sequence segments the state scan of problem `p` uses (1: one
  * serial scan over all chunks), or 0 when `p` fails validation.  The

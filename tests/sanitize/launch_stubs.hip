@@ -18,4 +18,5 @@ gdr_status launch_scan32_f32(const Prob&, ScanArgs&, hipStream_t) { return GDR_E
 gdr_status launch_decode(int, int, int, bool, bool, DecodeArgs&, hipStream_t) {
   return GDR_ERR_HIP;
 }
+gdr_status launch_check(const Prob&, CheckArgs&, hipStream_t) { return GDR_ERR_HIP; }
 }  // namespace gdr

@@ -125,6 +125,32 @@ def test_alignment(lib):
         assert binding.STATUS_NAMES[call_fwd(lib, base(), **kw)] == "GDR_ERR_ALIGN", kw
 
 
+def call_check(lib, prob, q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, flags=6 * A):
+    return lib.gdr_check_inputs(None if prob is None else ctypes.byref(prob), q, k, v, g, beta,
+                                flags, None)
+
+
+def test_check_inputs_validates(lib):
+    name = lambda st: binding.STATUS_NAMES[st]
+    assert name(call_check(lib, None)) == "GDR_ERR_NULL"
+    assert name(call_check(lib, base(B=0))) == "GDR_ERR_SHAPE"
+    assert name(call_check(lib, base(K=96))) == "GDR_ERR_UNSUPPORTED"
+    assert name(call_check(lib, base(chunk=-64))) == "GDR_ERR_ARG"
+    p = base()
+    p.qkv_dtype = 5
+    assert name(call_check(lib, p)) == "GDR_ERR_DTYPE"
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(beta=None),
+               dict(flags=None)):
+        assert name(call_check(lib, base(), **kw)) == "GDR_ERR_NULL", kw
+    for kw in (dict(q=A + 8), dict(g=4 * A + 4), dict(beta=5 * A + 8), dict(flags=6 * A + 2)):
+        assert name(call_check(lib, base(), **kw)) == "GDR_ERR_ALIGN", kw
+    # the flags word must not overlap an input: q holds 1*100*2*128*2 bytes
+    assert name(call_check(lib, base(), flags=A + 4096)) == "GDR_ERR_ALIAS"
+    assert name(call_check(lib, base(), flags=5 * A + 1596)) == "GDR_ERR_ALIAS"  # last beta
+    assert name(call_check(lib, base(per_channel=True), flags=4 * A + 400 * 512 - 4)) == \
+        "GDR_ERR_ALIAS"                                                # last per-channel g
+
+
 def test_workspace_checks(lib):
     p = base()
     need = gdr.workspace_size(p)
@@ -342,6 +368,10 @@ def test_binding_checks_outputs_and_workspace(lib):
                            out=(torch.empty(1, 40, 4, 32), s))
     with pytest.raises(ValueError, match="on a GPU"):
         gdr.gdr_chunk_scan(*args, torch.empty(need, dtype=torch.uint8), out=(o, s))
+    with pytest.raises(ValueError, match="on a GPU"):
+        gdr.gdr_check_inputs(*args)
+    with pytest.raises(TypeError, match="flags must be an int32"):
+        gdr.gdr_check_inputs(*args, flags=torch.zeros(1, dtype=torch.int64))
     d = {k_: v_[:, 0].contiguous() for k_, v_ in t.items()}
     dargs = (d["q"], d["k"], d["v"], d["g"], d["beta"])
     st = torch.zeros(1, 4, 64, 64)
