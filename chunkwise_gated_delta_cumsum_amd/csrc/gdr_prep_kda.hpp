@@ -36,6 +36,13 @@
 
 namespace gdr {
 
+// The in-block cumsums are kept in log2 units (g / ln 2), so that every
+// factor below is one exp2 (a single v_exp_f32) of a sum or difference of
+// them.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Threshold of the fp32 middle-row factorisation of a diagonal block.
 constexpr float kDiagExpLimit = 80.f;
 // Within e^+-4 of the middle row every factor of a diagonal block's operands
@@ -59,7 +66,9 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
-template <int K, int C, class P, bool DUMP>
+// NORM: L2-normalise the q and k rows (qk_l2norm); a template argument so
+// that the unnormalised kernel carries no row-factor products.
+template <int K, int C, class P, bool DUMP, bool NORM>
 __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
   using in_t = typename P::in_t;
   using frag_t = typename P::frag_t;
@@ -169,12 +178,20 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
       kr[kb] = P::load_raw8(reinterpret_cast<const in_t*>(stg + (16 + r) * QSR) + 32 * kb + 8 * grp);
     }
   }
+  // rows past T: zero q and k once, here, rather than at every use
+  if (!valid) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qr[kb] = raw_t{};
+      kr[kb] = raw_t{};
+    }
+  }
   // optional L2 normalisation of this lane's q and k row: its channels are
   // spread over the lanes r, r + 16, r + 32, r + 48 (grp), 8 per k block.
   // The raw values stay in registers; the row factors rsqrt(sum x^2 + 1e-6)
-  // multiply them in fp32 where they are converted below (1 when off).
+  // multiply them in fp32 where they are converted below.
   float fq = 1.f, fk = 1.f;
-  if (a.l2norm) {
+  if constexpr (NORM) {
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -199,8 +216,8 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      s[kb][j] = row_scan16(valid ? glo[kb][j] : 0.f);
-      s[kb][4 + j] = row_scan16(valid ? ghi[kb][j] : 0.f);
+      s[kb][j] = row_scan16(valid ? glo[kb][j] * kLog2e : 0.f);
+      s[kb][4 + j] = row_scan16(valid ? ghi[kb][j] * kLog2e : 0.f);
     }
   if (r == 15 || r == 7) {
     float* dst = (r == 15 ? sTot : sMid) + I * K;
@@ -226,18 +243,18 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
     float* rs = a.rs + (size_t)cid * 256;
     for (int it = part; it < 2 * NB + NPAIR + 1; it += NT / K) {
       if (it < NB) {
-        sPf[it * K + d] = __expf(pre(it));
+        sPf[it * K + d] = ex2(pre(it));
       } else if (it < 2 * NB) {
-        sSf[(it - NB) * K + d] = __expf(pre(NB) - pre(it - NB + 1));
+        sSf[(it - NB) * K + d] = ex2(pre(NB) - pre(it - NB + 1));
       } else if (it < 2 * NB + NPAIR) {
         // pair p = I2 (I2 - 1) / 2 + J2 with J2 < I2
         const int p = it - 2 * NB;
         int I2 = 1;
         while ((I2 + 1) * I2 / 2 <= p) ++I2;
         const int J2 = p - I2 * (I2 - 1) / 2;
-        sCf[p * K + d] = __expf(pre(I2) - pre(J2 + 1));
+        sCf[p * K + d] = ex2(pre(I2) - pre(J2 + 1));
       } else {
-        rs[C + row_of_chan(d)] = __expf(pre(NB));   // in the state's row order
+        rs[C + row_of_chan(d)] = ex2(pre(NB));   // in the state's row order
       }
     }
     for (int e = tid; e < C; e += NT) rs[e] = 1.f;
@@ -261,8 +278,14 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
   // scheduling fences keep the parts from overlapping): held together, the
   // rows of every part would need more registers than three workgroups per
   // CU leave.
-  auto qv_of = [&](int kb, int j) { return valid ? P::raw_f32(qr[kb], j) * fq : 0.f; };
-  auto kv_of = [&](int kb, int j) { return valid ? P::raw_f32(kr[kb], j) * fk : 0.f; };
+  auto qv_of = [&](int kb, int j) {
+    const float x = P::raw_f32(qr[kb], j);
+    return NORM ? x * fq : x;
+  };
+  auto kv_of = [&](int kb, int j) {
+    const float x = P::raw_f32(kr[kb], j);
+    return NORM ? x * fk : x;
+  };
   auto f4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -272,7 +295,7 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
       float kl[8], ql[8], qx[8], kx[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float el = __expf(s[kb][j]);
+        const float el = ex2(s[kb][j]);
         kl[j] = kv_of(kb, j) * el;
         ql[j] = qv_of(kb, j) * el;
         const float pf = j < 4 ? pa[j] : pb[j - 4];   // exp(gamma_i) = exp(s) exp(pre[I])
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float s15 = j < 4 ? t15a[j] : t15b[j - 4];
-        ke[j] = kv_of(kb, j) * __expf(s15 - s[kb][j]);
+        ke[j] = kv_of(kb, j) * ex2(s15 - s[kb][j]);
         // exp(gamma_last - gamma_i) = exp(s15 - s) exp(pre[NB] - pre[I+1])
         wx[j] = bv * ke[j] * (j < 4 ? wa[j] : wb[j - 4]);
       }
@@ -309,9 +332,9 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float dl = s[kb][j] - (j < 4 ? tma[j] : tmb[j - 4]);
-        far |= !(fabsf(dl) <= kDiagExpLimit);
-        wide |= !(fabsf(dl) <= kDiagF16Limit);
-        const float dm = __expf(dl), dmi = __expf(-dl);
+        far |= !(fabsf(dl) <= kDiagExpLimit * kLog2e);
+        wide |= !(fabsf(dl) <= kDiagF16Limit * kLog2e);
+        const float dm = ex2(dl), dmi = ex2(-dl);
         const float kv = kv_of(kb, j);
         a1[j] = kv * dm;
         b1[j] = kv * dmi;
@@ -372,8 +395,8 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float qv = valid ? P::raw_f32(qr2[kb], j) * fq : 0.f;
-          const float kv = valid ? P::raw_f32(kr2[kb], j) * fk : 0.f;
+          const float qv = valid ? (NORM ? P::raw_f32(qr2[kb], j) * fq : P::raw_f32(qr2[kb], j)) : 0.f;
+          const float kv = valid ? (NORM ? P::raw_f32(kr2[kb], j) * fk : P::raw_f32(kr2[kb], j)) : 0.f;
           const float kj = __shfl(kv, src, 64);
           const float sj = __shfl(s2[kb][j], src, 64);
           const float e = __expf(s2[kb][j] - sj);
@@ -410,7 +433,7 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
           const int d = 32 * kb + 8 * grp + j;
           float pre = 0.f;
           for (int m = 0; m < I; ++m) pre += sTot[m * K + d];
-          dg[d] = pre + s[kb][j];
+          dg[d] = (pre + s[kb][j]) * kLn2;   // natural units
         }
     }
   }

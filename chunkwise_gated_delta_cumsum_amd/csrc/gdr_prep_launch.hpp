@@ -13,8 +13,11 @@ gdr_status launch_prep_k(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
   const unsigned grid = (unsigned)(units8 * r.HV);
   constexpr unsigned block = C * 4;   // one wave per 16-row block
   if constexpr (PERCH) {
-    if (dump) return launch(chunk_prep_kda_kernel<K, C, P, true>, grid, block, a, s);
-    return launch(chunk_prep_kda_kernel<K, C, P, false>, grid, block, a, s);
+    if (r.l2norm)
+      return dump ? launch(chunk_prep_kda_kernel<K, C, P, true, true>, grid, block, a, s)
+                  : launch(chunk_prep_kda_kernel<K, C, P, false, true>, grid, block, a, s);
+    return dump ? launch(chunk_prep_kda_kernel<K, C, P, true, false>, grid, block, a, s)
+                : launch(chunk_prep_kda_kernel<K, C, P, false, false>, grid, block, a, s);
   } else {
     if (dump) return launch(chunk_prep_kernel<K, C, P, true>, grid, block, a, s);
     return launch(chunk_prep_kernel<K, C, P, false>, grid, block, a, s);
