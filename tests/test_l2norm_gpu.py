@@ -49,10 +49,11 @@ def test_chunk_fwd_in_kernel_l2norm(gpu_lib, w, segs):
     check(o.cpu().numpy(), s.cpu().numpy(), ro, rs, w.dtype, f"{w.name} T={w.T}")
 
 
-def test_in_kernel_l2norm_large_rows(gpu_lib):
+@pytest.mark.parametrize("idx", [1, 2], ids=["row_decay", "per_channel"])
+def test_in_kernel_l2norm_large_rows(gpu_lib, idx):
     """Raw rows far from unit length (x 40) normalise to the same result."""
     import torch
-    w = WORKLOADS[1].with_(T=200, normalize_qk=False)
+    w = WORKLOADS[idx].with_(B=1, T=200, normalize_qk=False)
     inp = make_inputs(w)
     t = to_device(inp)
     q = (t["q"].float() * 40).to(t["q"].dtype)
@@ -64,7 +65,7 @@ def test_in_kernel_l2norm_large_rows(gpu_lib):
     kr = k.float().cpu().numpy().astype(np.float64)
     ro, rs = oracle.recurrence(oracle.l2norm_rows(qr), oracle.l2norm_rows(kr), inp.v, inp.g,
                                inp.beta, inp.scale, None)
-    check(o.cpu().numpy(), s.cpu().numpy(), ro, rs, w.dtype, "raw rows x40")
+    check(o.cpu().numpy(), s.cpu().numpy(), ro, rs, w.dtype, f"raw rows x40 {w.name}")
 
 
 @pytest.mark.parametrize("w", [WORKLOADS[3].with_(B=3, T=1, s0_std=0.1, normalize_qk=False),
