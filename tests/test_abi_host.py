@@ -36,6 +36,23 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(binding.EXPORTED)
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/gdr.h compiles as strict C99 (the ABI carries no C++ types)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_gdr.c"
+    src.write_text('#include "gdr.h"\n'
+                   "int probe(const gdr_problem* p, void* s) {\n"
+                   "  uint32_t* f = 0;\n"
+                   "  return (int)gdr_check_inputs(p, 0, 0, 0, 0, 0, f, s) + (int)GDR_CHECK_DECAY_RANGE"
+                   " + (int)gdr_chunk_fwd_workspace_size(p) + gdr_version();\n}\n")
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                           "-I", os.path.join(ROOT, "include"), "-c", str(src),
+                           "-o", str(tmp_path / "use_gdr.o")])
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
