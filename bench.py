@@ -365,10 +365,12 @@ def main():
         return
     dev = torch.device("cuda", 0)
 
+    half = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+
     def to_dev(a):
         import numpy as np
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if a.dtype == np.uint16:          # 16-bit storage: bf16 or fp16 bits
+            return torch.from_numpy(a.view(np.int16)).view(half).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     base = dict(q=to_dev(inp.q_dev), k=to_dev(inp.k_dev), v=to_dev(inp.v_dev),

@@ -11,4 +11,4 @@ from .binding import (GDR_BF16, GDR_F32, CHECK_BITS, EXPORTED, GdrError, GdrProb
                       problem,
                       scan_segments, scan_slab, status_string, workspace_size)
 
-__version__ = "0.4.0"
+__version__ = "0.5.0"

@@ -17,8 +17,8 @@ from typing import Dict, Optional, Tuple
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdr.so")
 
-GDR_F32, GDR_BF16 = 0, 1
-DTYPES = {"fp32": GDR_F32, "bf16": GDR_BF16}   # gdr_dtype of q/k/v and of o
+GDR_F32, GDR_BF16, GDR_F16 = 0, 1, 2
+DTYPES = {"fp32": GDR_F32, "bf16": GDR_BF16, "fp16": GDR_F16}   # gdr_dtype of q/k/v and of o
 RULES = {"delta": 0, "linear": 1}   # gdr_rule: gated delta rule, decayed linear attention
 GDR_OK = 0
 STATUS_NAMES = {
@@ -133,14 +133,22 @@ def _ptr(t) -> Optional[int]:
 
 def _torch_dtype(name: str):
     import torch
-    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+    return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[name]
+
+
+def _dtype_name(t) -> str:
+    """The gdr dtype name of a q/k/v tensor (float32, bfloat16 or float16)."""
+    import torch
+    names = {torch.float32: "fp32", torch.bfloat16: "bf16", torch.float16: "fp16"}
+    if t.dtype not in names:
+        raise TypeError(f"q/k/v must be float32, bfloat16 or float16, got {t.dtype}")
+    return names[t.dtype]
 
 
 def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
                   qk_l2norm=False, rule="delta", o_dtype="fp32") -> GdrProblem:
     import torch
-    if q.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
+    _dtype_name(q)
     if k.dtype != q.dtype or (v is not None and v.dtype != q.dtype):
         raise TypeError("q, k and v must share one dtype")
     if q.dim() != 4 or k.shape != q.shape:
@@ -165,7 +173,7 @@ def _problem_from(q, k, v, g, beta, chunk, scale, segments=0, slab=0,
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
     return problem(B, T, H, HV, K, V, chunk=chunk, per_channel=per_channel, scale=scale,
-                   dtype="fp32" if q.dtype == torch.float32 else "bf16", segments=segments,
+                   dtype=_dtype_name(q), segments=segments,
                    slab=slab, qk_l2norm=qk_l2norm, rule=rule, o_dtype=o_dtype)
 
 
@@ -228,12 +236,12 @@ def gdr_chunk_fwd(q, k, v, g, beta, initial_state=None, chunk: int = 0,
                   ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunkwise gated delta rule forward on the GPU.
 
-    q, k: [B, T, H, K]; v: [B, T, HV, V] (float32 or bfloat16, one dtype);
+    q, k: [B, T, H, K]; v: [B, T, HV, V] (float32, bfloat16 or float16, one dtype);
     g: [B, T, HV] or [B, T, HV, K] float32 log-decay; beta: [B, T, HV] float32;
     initial_state: [B, HV, K, V] float32 or None.  scale defaults to K**-0.5;
     chunk is 32, 64 or 128, or 0 for the automatic choice (64).
     Returns (o [B, T, HV, V], final_state [B, HV, K, V] float32 or None); o is
-    float32, or bfloat16 with ``o_dtype="bf16"`` (the fp32 result rounded
+    float32, or bfloat16 / float16 with ``o_dtype="bf16"`` / ``"fp16"`` (the fp32 result rounded
     once, to nearest even).
     ``workspace`` (uint8, at least workspace_size bytes) and ``out`` = (o, S)
     may be passed to avoid allocations.  ``segments`` > 0 asks for that many
@@ -435,10 +443,10 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
                     ) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """One decode step (one token per sequence) on the GPU.
 
-    q, k: [B, H, K]; v: [B, HV, V] (float32 or bfloat16, one dtype);
+    q, k: [B, H, K]; v: [B, HV, V] (float32, bfloat16 or float16, one dtype);
     g: [B, HV] or [B, HV, K] float32 log-decay; beta: [B, HV] float32;
     state: [B, HV, K, V] float32 or None (zero state).  scale defaults to
-    K**-0.5.  Returns (o [B, HV, V] float32 (bfloat16 with o_dtype="bf16"),
+    K**-0.5.  Returns (o [B, HV, V] float32 (bfloat16 / float16 with o_dtype),
     new state [B, HV, K, V] float32).
     With ``inplace`` the new state overwrites ``state``; ``out`` = (o, S) may
     be passed to avoid allocations.  ``slab`` (32, 64 or 128) sets the state
@@ -449,8 +457,7 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     lib = load()
     dev = q.device
     _check_tensors(dev, q=q, k=k, v=v, g=g, beta=beta, state=state)
-    if q.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
+    _dtype_name(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
     if q.dim() != 3 or k.shape != q.shape:
@@ -474,7 +481,7 @@ def gdr_decode_step(q, k, v, g, beta, state=None, scale: Optional[float] = None,
     if inplace and state is None:
         raise ValueError("inplace needs a state")
     prob = problem(B, 1, H, HV, K, V, per_channel=per_channel, scale=scale,
-                   dtype="fp32" if q.dtype == torch.float32 else "bf16", slab=slab,
+                   dtype=_dtype_name(q), slab=slab,
                    qk_l2norm=qk_l2norm, rule=rule, o_dtype=o_dtype)
     odt = _torch_dtype(o_dtype)
     if out is not None:

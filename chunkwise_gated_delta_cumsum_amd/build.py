@@ -23,7 +23,10 @@ SOURCES = [os.path.join(CSRC, f) for f in (
     "gdr_api.hip", "gdr_launch_prep.hip", "gdr_launch_prep128.hip", "gdr_launch_scan_f16.hip",
     "gdr_launch_scan_lin.hip", "gdr_launch_scan_f32.hip", "gdr_launch_scan128_f16.hip",
     "gdr_launch_scan128_f32.hip", "gdr_launch_prep32.hip", "gdr_launch_scan32_f16.hip",
-    "gdr_launch_scan32_f32.hip", "gdr_launch_decode.hip", "gdr_launch_check.hip")]
+    "gdr_launch_scan32_f32.hip", "gdr_launch_decode.hip", "gdr_launch_check.hip",
+    "gdr_launch_prep_h16.hip", "gdr_launch_prep128_h16.hip", "gdr_launch_prep32_h16.hip",
+    "gdr_launch_scan_h16.hip", "gdr_launch_scan_lin_h16.hip", "gdr_launch_scan128_h16.hip",
+    "gdr_launch_scan32_h16.hip")]
 OBJDIR = os.path.join(ROOT, "_build")
 DEPS = SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + [
     os.path.join(INCLUDE, "gdr.h")]

@@ -78,8 +78,10 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   if (p->B < 1 || p->T < 1 || p->H < 1 || p->HV < 1 || p->K < 1 || p->V < 1 ||
       p->HV % p->H != 0)
     return GDR_ERR_SHAPE;
-  if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
-  if (p->o_dtype != GDR_F32 && p->o_dtype != GDR_BF16) return GDR_ERR_DTYPE;
+  if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16 && p->qkv_dtype != GDR_F16)
+    return GDR_ERR_DTYPE;
+  if (p->o_dtype != GDR_F32 && p->o_dtype != GDR_BF16 && p->o_dtype != GDR_F16)
+    return GDR_ERR_DTYPE;
   if (p->g_per_channel != 0 && p->g_per_channel != 1) return GDR_ERR_ARG;
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1) return GDR_ERR_ARG;
   if (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) return GDR_ERR_ARG;
@@ -98,11 +100,12 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   r.N = (p->T + r.C - 1) / r.C;
   r.perch = p->g_per_channel == 1;
   r.f32 = p->qkv_dtype == GDR_F32;
+  r.h16 = p->qkv_dtype == GDR_F16;
   r.scale = p->scale;
   r.l2norm = p->qk_l2norm == 1;
   r.linear = p->rule == GDR_RULE_LINEAR;
   r.es = r.f32 ? 4 : 2;
-  r.obf16 = p->o_dtype == GDR_BF16;
+  r.ofmt = p->o_dtype;   // GDR_F32, GDR_BF16, GDR_F16 = kOutF32, kOutBF16, kOutF16
   if (p->scan_segments < 0) return GDR_ERR_ARG;
   if (p->scan_slab != 0 && p->scan_slab != 32 && p->scan_slab != 64) return GDR_ERR_ARG;
   // 128-row chunks are built with one slab width per key dimension: 32
@@ -184,7 +187,7 @@ Spans spans(const Prob& r, const void* q, const void* k, const void* v, const fl
   s.g = {g, tok * r.HV * (r.perch ? r.K : 1) * sizeof(float)};
   s.beta = {beta, tok * r.HV * sizeof(float)};
   s.s0 = {s0, (size_t)r.B * r.HV * r.K * r.V * sizeof(float)};
-  s.o = {o, tok * r.HV * r.V * (r.obf16 ? 2 : 4)};
+  s.o = {o, tok * r.HV * r.V * (r.ofmt != kOutF32 ? 2 : 4)};
   s.sT = {sT, (size_t)r.B * r.HV * r.K * r.V * sizeof(float)};
   s.ws = {ws, ws_bytes};
   return s;
@@ -214,6 +217,12 @@ gdr_status check_device() {
 }
 
 gdr_status launch_scan(const Prob& r, ScanArgs& a, hipStream_t s) {
+  if (r.h16) {
+    if (r.C == 128) return launch_scan128_h16(r, a, s);
+    if (r.C == 32) return launch_scan32_h16(r, a, s);
+    if (r.linear && r.bv == 64) return launch_scan_h16_linear(r, a, s);
+    return launch_scan_h16(r, a, s);
+  }
   if (r.C == 128) return r.f32 ? launch_scan128_f32(r, a, s) : launch_scan128_f16(r, a, s);
   if (r.C == 32) return r.f32 ? launch_scan32_f32(r, a, s) : launch_scan32_f16(r, a, s);
   if (r.f32) return launch_scan_f32(r, a, s);
@@ -243,7 +252,7 @@ ScanArgs scan_args(const Prob& r, const void* q, const void* k, const void* v,
   char* base = static_cast<char*>(const_cast<void*>(ws));
   ScanArgs a;
   a.q = q; a.k = k; a.v = v; a.s0 = s0; a.o = o; a.sT = sT;
-  a.o_bf16 = r.obf16 ? 1 : 0;
+  a.o_fmt = r.ofmt;
   // In place (final_state == initial_state) with sequence segments, the
   // last segment's workgroups write the final state while workgroups of
   // other segments may not yet have read their columns of the initial
@@ -342,8 +351,10 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   if (p->B < 1 || p->T != 1 || p->H < 1 || p->HV < 1 || p->K < 1 || p->V < 1 ||
       p->HV % p->H != 0)
     return GDR_ERR_SHAPE;
-  if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16) return GDR_ERR_DTYPE;
-  if (p->o_dtype != GDR_F32 && p->o_dtype != GDR_BF16) return GDR_ERR_DTYPE;
+  if (p->qkv_dtype != GDR_F32 && p->qkv_dtype != GDR_BF16 && p->qkv_dtype != GDR_F16)
+    return GDR_ERR_DTYPE;
+  if (p->o_dtype != GDR_F32 && p->o_dtype != GDR_BF16 && p->o_dtype != GDR_F16)
+    return GDR_ERR_DTYPE;
   if ((p->g_per_channel != 0 && p->g_per_channel != 1) ||
       (p->qk_l2norm != 0 && p->qk_l2norm != 1) ||
       (p->rule != GDR_RULE_DELTA && p->rule != GDR_RULE_LINEAR) || !std::isfinite(p->scale))
@@ -365,7 +376,7 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   const Span sb = {beta, heads * sizeof(float)};
   const Span si = {state_in, heads * p->K * p->V * sizeof(float)};
   const Span so = {state_out, si.n};
-  const Span sO = {o, heads * p->V * (p->o_dtype == GDR_BF16 ? 2 : 4)};
+  const Span sO = {o, heads * p->V * (p->o_dtype != GDR_F32 ? 2 : 4)};
   if (out_overlaps(sO, {sq, sk, sv, sg, sb, si, so})) return GDR_ERR_ALIAS;
   if (out_overlaps(so, {sq, sk, sv, sg, sb})) return GDR_ERR_ALIAS;
   if (state_in && state_in != state_out && overlap(si, so)) return GDR_ERR_ALIAS;
@@ -374,15 +385,14 @@ gdr_status gdr_decode_step(const gdr_problem* p, const void* q, const void* k, c
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.s_in = state_in; a.s_out = state_out; a.o = o;
-  a.o_bf16 = p->o_dtype == GDR_BF16 ? 1 : 0;
+  a.o_fmt = p->o_dtype;
   a.B = p->B; a.H = p->H; a.HV = p->HV;
   a.scale = p->scale;
   a.l2norm = p->qk_l2norm;
   a.linear = p->rule == GDR_RULE_LINEAR;
-  const bool f32 = p->qkv_dtype == GDR_F32;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int vb = decode_columns(p);
-  return launch_decode(p->K, p->V, vb, p->g_per_channel == 1, f32, a, hs);
+  return launch_decode(p->K, p->V, vb, p->g_per_channel == 1, p->qkv_dtype, a, hs);
 }
 
 gdr_status gdr_check_inputs(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -409,8 +419,8 @@ gdr_status gdr_check_inputs(const gdr_problem* p, const void* q, const void* k, 
   a.nbeta = tok * r.HV;
   a.B = r.B; a.T = r.T; a.HV = r.HV; a.K = r.K; a.C = r.C; a.N = r.N;
   a.perch = r.perch;
-  a.bf16 = !r.f32;
-  a.qk_range = !r.f32 && !r.l2norm;
+  a.fmt = r.f32 ? 0 : (r.h16 ? 2 : 1);
+  a.qk_range = a.fmt == 1 && !r.l2norm;   // bf16 values can exceed the fp16 range
   a.decay = !r.f32;
   return launch_check(r, a, static_cast<hipStream_t>(stream));
 }
@@ -545,6 +555,6 @@ int gdr_chunk_scan_slab(const gdr_problem* p) {
   return r.bv;
 }
 
-int gdr_version(void) { return 400; }   // 0.4.0: gdr_check_inputs added
+int gdr_version(void) { return 500; }   // 0.5.0: fp16 inputs and o (GDR_F16)
 
 }  // extern "C"

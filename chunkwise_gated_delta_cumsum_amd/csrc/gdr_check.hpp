@@ -2,7 +2,7 @@
 // that records, as bits of one device word, whether they break the numeric
 // preconditions of the 16-bit path (see the numerics notes in gdr.h).
 //
-// * Non-finite values in q, k, v, g or beta.
+// * Non-finite values in q, k, v, g or beta (fp32, bf16 or fp16 encodings).
 // * bf16 q, k or v whose magnitude rounds to infinity in fp16 (|x| >= 65520
 //   rounds up past 65504; the largest bf16 below that is 65280, the
 //   smallest above it 65536): the MFMA operands are fp16, and bf16 -> fp16
@@ -38,8 +38,8 @@ struct CheckArgs {
   size_t nqk, nv, nbeta;  // elements of q (= of k), of v, of beta
   int B, T, HV, K, C, N;  // shapes; N = ceil(T / C) chunks per sequence
   bool perch;             // g is [B, T, HV, K] (else [B, T, HV])
-  bool bf16;              // q, k, v are bf16 (else fp32: only finiteness)
-  bool qk_range;          // check q and k against the fp16 range
+  int fmt;                // q, k, v: 0 fp32, 1 bf16, 2 fp16
+  bool qk_range;          // check q and k against the fp16 range (bf16 only)
   bool decay;             // check the positive g sums (the 16-bit path)
 };
 

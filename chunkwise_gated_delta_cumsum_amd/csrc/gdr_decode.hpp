@@ -37,8 +37,8 @@ struct DecodeArgs {
   const float* beta;     // [B, HV]
   const float* s_in;     // [B, HV, K, V] or null (zero state)
   float* s_out;          // [B, HV, K, V]; may equal s_in
-  void* o;               // [B, HV, V] fp32, or bf16 when o_bf16
-  int o_bf16;
+  void* o;               // [B, HV, V] in the format o_fmt
+  int o_fmt;             // kOutF32, kOutBF16 or kOutF16
   int B, H, HV;
   float scale;
   int l2norm;            // 1: L2-normalise q and k first
@@ -54,6 +54,10 @@ __device__ __forceinline__ float decode_in<float>(const void* p, size_t i) {
 template <>
 __device__ __forceinline__ float decode_in<uint16_t>(const void* p, size_t i) {
   return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);   // bf16 bits
+}
+template <>
+__device__ __forceinline__ float decode_in<_Float16>(const void* p, size_t i) {
+  return (float)static_cast<const _Float16*>(p)[i];
 }
 
 template <int K, int V, int VB, bool PERCH, class IN>
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * c4);
   const f32x4 u = a.linear ? vv : vv - A;
   if (wave == 0 && lane < LPR)
-    store_o4(a.o, (size_t)bh * V + v0 + 4 * c4, a.scale * (Bq + (bt * sqk) * u), a.o_bf16 != 0);
+    store_o4(a.o, (size_t)bh * V + v0 + 4 * c4, a.scale * (Bq + (bt * sqk) * u), a.o_fmt);
   const f32x4 bu = (bt * srk) * u;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {

@@ -13,6 +13,7 @@
 // every product use the same k slots, so the hardware's own k order inside
 // an instruction does not matter.
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,11 +81,21 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // wherever its values enter a product or an fp16 operand.
 constexpr float kL2NormEps = 1e-6f;
 
-// Sum of squares of the input elements in 16 bytes (8 bf16 or 4 fp32).
+// Sum of squares of the input elements in 16 bytes (8 fp16, 8 bf16 or 4 fp32).
 template <class IN>
 __device__ __forceinline__ float sumsq16(u32x4 v) {
   float s = 0.f;
-  if constexpr (sizeof(IN) == 2) {
+  if constexpr (std::is_same_v<IN, _Float16>) {
+    // each half through a scalar bit cast (a bit cast of v[i] to a vector of
+    // two halves inside this unrolled loop compiled to four copies of v[0])
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+      const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+      s += lo * lo + hi * hi;
+    }
+  } else if constexpr (sizeof(IN) == 2) {   // bf16 bits
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
@@ -108,12 +119,26 @@ __device__ __forceinline__ u16x4 bf16x4_rne(f32x4 x) {
   return r;
 }
 
-// Stores 4 consecutive o values at element offset e of o (fp32, or bf16
-// when bf16 is set), streamed: o is not read again on the device.
-__device__ __forceinline__ void store_o4(void* o, size_t e, f32x4 x, bool bf16) {
-  if (bf16)
+// Four fp32 values rounded to fp16 (nearest even), as the bits of 8 bytes.
+__device__ __forceinline__ u16x4 f16x4_rne(f32x4 x) {
+  u16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint16_t, (_Float16)x[i]);
+  return r;
+}
+
+// Storage formats of o (gdr_problem::o_dtype).
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2;
+
+// Stores 4 consecutive o values at element offset e of o (fp32, or rounded
+// once to bf16 or fp16 by fmt), streamed: o is not read again on the device.
+__device__ __forceinline__ void store_o4(void* o, size_t e, f32x4 x, int fmt) {
+  if (fmt == kOutBF16)
     __builtin_nontemporal_store(bf16x4_rne(x), reinterpret_cast<u16x4*>(
                                                    static_cast<uint16_t*>(o) + e));
+  else if (fmt == kOutF16)
+    __builtin_nontemporal_store(f16x4_rne(x), reinterpret_cast<u16x4*>(
+                                                  static_cast<uint16_t*>(o) + e));
   else
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(static_cast<float*>(o) + e));
 }
@@ -149,12 +174,16 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
 
 // ---- precision policies ---------------------------------------------------
 // F16: bf16 inputs, fp16 MFMA operands, fp16 workspace fragments.
+// H16: fp16 inputs, used as they are as fp16 MFMA operands; fp16 workspace.
 // F32: fp32 inputs, fp32 MFMA, fp32 workspace fragments.
+// gfrag_t: the operand type of the decayed-dot Gram products, which take
+// the raw input values (products of two 16-bit inputs are exact in fp32).
 struct PolicyF16 {
   using in_t = uint16_t;   // bf16 bits
   using frag_t = half8;
   using ws_t = _Float16;
   using raw_t = u16x8;     // 8 input elements as loaded, before conversion
+  using gfrag_t = bf16x8;
   static constexpr bool kF32 = false;
   __device__ static __forceinline__ raw_t load_raw(const in_t* row, int grp) {
     const u16x4 lo = *reinterpret_cast<const u16x4*>(row + 4 * grp);
@@ -217,11 +246,54 @@ struct PolicyF16 {
   }
 };
 
+struct PolicyH16 {
+  using in_t = _Float16;
+  using frag_t = half8;
+  using ws_t = _Float16;
+  using raw_t = u16x8;     // fp16 bits as loaded
+  using gfrag_t = half8;
+  static constexpr bool kF32 = false;
+  __device__ static __forceinline__ float h(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+  __device__ static __forceinline__ raw_t load_raw(const in_t* row, int grp) {
+    const u16x4 lo = *reinterpret_cast<const u16x4*>(row + 4 * grp);
+    const u16x4 hi = *reinterpret_cast<const u16x4*>(row + 16 + 4 * grp);
+    return raw_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static __forceinline__ raw_t load_raw8(const in_t* p) {
+    return *reinterpret_cast<const raw_t*>(p);
+  }
+  __device__ static __forceinline__ frag_t from_raw(raw_t x, bool valid) {
+    const frag_t f = __builtin_bit_cast(frag_t, x);
+    return valid ? f : frag_t{};
+  }
+  __device__ static __forceinline__ frag_t frag_from_raw(raw_t x) {
+    return __builtin_bit_cast(frag_t, x);
+  }
+  __device__ static __forceinline__ float in_to_f32(in_t x) { return (float)x; }
+  __device__ static __forceinline__ float raw_f32(raw_t x, int i) { return h(x[i]); }
+  __device__ static __forceinline__ frag_t frag_scaled(raw_t x, float f) {
+    frag_t r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)(h(x[i]) * f);
+    return r;
+  }
+  __device__ static __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {
+    return PolicyF16::mma16(a, b, c);
+  }
+  __device__ static __forceinline__ frag_t make(const float* v) { return PolicyF16::make(v); }
+  __device__ static __forceinline__ frag_t make2(f32x4 lo, f32x4 hi) {
+    return PolicyF16::make2(lo, hi);
+  }
+};
+
 struct PolicyF32 {
   using in_t = float;
   using frag_t = f32x8;
   using ws_t = float;
   using raw_t = f32x8;
+  using gfrag_t = f32x8;
   static constexpr bool kF32 = true;
   __device__ static __forceinline__ raw_t load_raw(const in_t* row, int grp) {
     const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);
@@ -282,6 +354,12 @@ __device__ __forceinline__ half8 frag_row_in(const uint16_t* row, int grp, Polic
     f[4 + i] = (_Float16)bf16_to_f32(hi[i]);
   }
   return f;
+}
+__device__ __forceinline__ half8 frag_row_in(const _Float16* row, int grp, PolicyH16) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 lo = *reinterpret_cast<const h4*>(row + 4 * grp);
+  const h4 hi = *reinterpret_cast<const h4*>(row + 16 + 4 * grp);
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 __device__ __forceinline__ f32x8 frag_row_in(const float* row, int grp, PolicyF32) {
   f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * grp);

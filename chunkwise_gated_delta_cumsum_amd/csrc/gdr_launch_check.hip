@@ -16,17 +16,22 @@ __global__ void check_clear_kernel(uint32_t* flags) {
   if (threadIdx.x == 0) *flags = 0u;
 }
 
-// bits of 8 bf16 values packed in 16 bytes
-__device__ __forceinline__ uint32_t bf16x8_bits(chk_u32x4 w, bool range) {
+// Bits of one 16-bit value (magnitude bits u): bf16 (inf/NaN from 0x7f80, fp16
+// overflow from 0x4780) or fp16 (inf/NaN from 0x7c00, never out of range).
+__device__ __forceinline__ uint32_t h16_bits(uint32_t u, int fmt, bool range) {
+  if (u >= (fmt == 2 ? 0x7c00u : 0x7f80u)) return GDR_CHECK_NONFINITE;
+  return (fmt == 1 && range && u >= 0x4780u) ? (uint32_t)GDR_CHECK_FP16_RANGE : 0u;
+}
+
+// bits of 8 16-bit values packed in 16 bytes
+__device__ __forceinline__ uint32_t h16x8_bits(chk_u32x4 w, int fmt, bool range) {
   uint32_t f = 0;
   const uint32_t part[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t u = (part[i] >> (16 * h)) & 0x7fffu;
-      if (u >= 0x7f80u) f |= GDR_CHECK_NONFINITE;
-      else if (range && u >= 0x4780u) f |= GDR_CHECK_FP16_RANGE;
+      f |= h16_bits((part[i] >> (16 * h)) & 0x7fffu, fmt, range);
     }
   }
   return f;
@@ -39,25 +44,24 @@ __device__ __forceinline__ uint32_t f32_bits(uint32_t u) {
 // One pass over a tensor of n elements (16-bit or fp32): 16-byte pieces
 // grid-strided, then the tail one element at a time (n need not be a
 // multiple of the piece).
-__device__ __forceinline__ uint32_t scan_tensor(const void* x, size_t n, bool bf16,
+__device__ __forceinline__ uint32_t scan_tensor(const void* x, size_t n, int fmt,
                                                 bool range, size_t tid, size_t nthreads) {
   uint32_t f = 0;
-  const size_t per = bf16 ? 8 : 4;
+  const bool h16 = fmt != 0;
+  const size_t per = h16 ? 8 : 4;
   const size_t npieces = n / per;
   const chk_u32x4* p = reinterpret_cast<const chk_u32x4*>(x);
   for (size_t i = tid; i < npieces; i += nthreads) {
     const chk_u32x4 w = __builtin_nontemporal_load(p + i);
-    if (bf16) {
-      f |= bf16x8_bits(w, range);
+    if (h16) {
+      f |= h16x8_bits(w, fmt, range);
     } else {
       f |= f32_bits(w[0]) | f32_bits(w[1]) | f32_bits(w[2]) | f32_bits(w[3]);
     }
   }
   for (size_t i = npieces * per + tid; i < n; i += nthreads) {
-    if (bf16) {
-      const uint32_t u = reinterpret_cast<const uint16_t*>(x)[i] & 0x7fffu;
-      if (u >= 0x7f80u) f |= GDR_CHECK_NONFINITE;
-      else if (range && u >= 0x4780u) f |= GDR_CHECK_FP16_RANGE;
+    if (h16) {
+      f |= h16_bits(reinterpret_cast<const uint16_t*>(x)[i] & 0x7fffu, fmt, range);
     } else {
       f |= f32_bits(reinterpret_cast<const uint32_t*>(x)[i]);
     }
@@ -69,10 +73,10 @@ __device__ __forceinline__ uint32_t scan_tensor(const void* x, size_t n, bool bf
 __global__ void __launch_bounds__(256) check_tensors_kernel(CheckArgs a) {
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t nth = (size_t)gridDim.x * blockDim.x;
-  uint32_t f = scan_tensor(a.q, a.nqk, a.bf16, a.qk_range, tid, nth);
-  f |= scan_tensor(a.k, a.nqk, a.bf16, a.qk_range, tid, nth);
-  f |= scan_tensor(a.v, a.nv, a.bf16, true, tid, nth);
-  f |= scan_tensor(a.beta, a.nbeta, false, false, tid, nth);
+  uint32_t f = scan_tensor(a.q, a.nqk, a.fmt, a.qk_range, tid, nth);
+  f |= scan_tensor(a.k, a.nqk, a.fmt, a.qk_range, tid, nth);
+  f |= scan_tensor(a.v, a.nv, a.fmt, true, tid, nth);
+  f |= scan_tensor(a.beta, a.nbeta, 0, false, tid, nth);
   flag_or(a.flags, f);
 }
 
@@ -126,7 +130,7 @@ gdr_status launch_check(const Prob& r, CheckArgs& a, hipStream_t s) {
   uint32_t* flags = a.flags;
   gdr_status st = launch(check_clear_kernel, 1, 64, flags, s);
   if (st != GDR_OK) return st;
-  const size_t per = a.bf16 ? 8 : 4;
+  const size_t per = a.fmt != 0 ? 8 : 4;
   size_t most = a.nqk > a.nv ? a.nqk : a.nv;
   if (a.nbeta > most) most = a.nbeta;
   st = launch(check_tensors_kernel, check_grid((most + per - 1) / per), 256, a, s);

@@ -6,6 +6,11 @@
 
 namespace gdr {
 gdr_status launch_prep(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
+  if (r.h16) {
+    if (r.C == 128) return launch_prep128_h16(r, a, dump, s);
+    if (r.C == 32) return launch_prep32_h16(r, a, dump, s);
+    return launch_prep_h16(r, a, dump, s);
+  }
   if (r.C == 128) return launch_prep128(r, a, dump, s);
   if (r.C == 32) return launch_prep32(r, a, dump, s);
   return launch_prep_c<64>(r, a, dump, s);

@@ -1,0 +1,8 @@
+// Launchers of the state-scan kernels for fp16 inputs, 128-row chunks.
+#include "gdr_scan_launch.hpp"
+
+namespace gdr {
+gdr_status launch_scan128_h16(const Prob& r, ScanArgs& a, hipStream_t s) {
+  return launch_scan_policy<PolicyH16, false, 128>(r, a, s);
+}
+}  // namespace gdr

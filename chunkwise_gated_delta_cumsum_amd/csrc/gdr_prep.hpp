@@ -401,8 +401,8 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kernel(PrepArgs a) {
   using ws_t = typename P::ws_t;
   using frag_t = typename P::frag_t;
   using raw_t = typename P::raw_t;
-  // Gram fragments: raw bf16 (exact bf16 x bf16 products) or fp32
-  using gfrag_t = std::conditional_t<P::kF32, f32x8, bf16x8>;
+  // Gram fragments: the raw 16-bit inputs (exact products) or fp32
+  using gfrag_t = typename P::gfrag_t;
   constexpr int NB = C / 16;                        // waves, one 16-row block each
   constexpr int NT = NB * 64;
   constexpr int KP = K + 16 / (int)sizeof(in_t);    // k tile row, +16 bytes

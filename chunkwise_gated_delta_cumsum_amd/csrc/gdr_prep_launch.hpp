@@ -30,13 +30,18 @@ gdr_status launch_prep_p(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
                    : launch_prep_k<128, C, PERCH, P>(r, a, dump, s);
 }
 
+template <int C, class P>
+gdr_status launch_prep_cp(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
+  return r.perch ? launch_prep_p<C, true, P>(r, a, dump, s)
+                 : launch_prep_p<C, false, P>(r, a, dump, s);
+}
+
+// fp32 and bf16 inputs; fp16 inputs have launcher units of their own
+// (gdr_launch_prep*_h16.hip)
 template <int C>
 gdr_status launch_prep_c(const Prob& r, PrepArgs& a, bool dump, hipStream_t s) {
-  if (r.f32)
-    return r.perch ? launch_prep_p<C, true, PolicyF32>(r, a, dump, s)
-                   : launch_prep_p<C, false, PolicyF32>(r, a, dump, s);
-  return r.perch ? launch_prep_p<C, true, PolicyF16>(r, a, dump, s)
-                 : launch_prep_p<C, false, PolicyF16>(r, a, dump, s);
+  if (r.f32) return launch_prep_cp<C, PolicyF32>(r, a, dump, s);
+  return launch_prep_cp<C, PolicyF16>(r, a, dump, s);
 }
 
 }  // namespace gdr

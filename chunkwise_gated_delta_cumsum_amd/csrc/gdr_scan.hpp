@@ -64,7 +64,7 @@ struct ScanArgs {
   const void* k;
   const void* v;
   const float* s0;
-  void* o;           // [B, T, HV, V] fp32, or bf16 when o_bf16
+  void* o;           // [B, T, HV, V] in the format o_fmt
   float* sT;
   const void* wt;
   const void* ah;
@@ -79,7 +79,7 @@ struct ScanArgs {
   void* phi;         // transitions [BH][nseg-1], each K x K in A-fragment order
                      // [K/16 row tiles][K/32 k blocks][64 lanes][8], workspace type
   float* eend;       // zero-start end states, tile order [BH][nseg-1][K*V]
-  int o_bf16;        // 1: o is stored as bf16
+  int o_fmt;         // kOutF32, kOutBF16 or kOutF16
   float* s0_copy;    // chain pass: when set, copy s0 here [BH][K][V] (the full
                      // pass then reads this copy: the state is updated in place)
 };
@@ -467,7 +467,7 @@ __device__ __forceinline__ void scan_wave(const ScanArgs& a, typename P::frag_t*
       const int t = n * C + CR * w + ORPI * i + lane / OLPR;
       if (t < T)
         store_o4(a.o, (((size_t)b * T + t) * a.HV + hv) * V + v0 + (lane % OLPR) * 4,
-                 orow_v[i], a.o_bf16 != 0);
+                 orow_v[i], a.o_fmt);
     }
   };
 

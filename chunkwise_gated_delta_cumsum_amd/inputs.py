@@ -21,7 +21,7 @@ beta and a state scaled by 0.1):
 * initial state = std * N(0, 1) on [B, HV, K, V] when std > 0, else absent.
 
 q, k and v are rounded once (round-to-nearest-even) to the storage dtype
-("fp32" or "bf16"); g, beta and the state are fp32.  Both sides then consume
+("fp32", "bf16" or "fp16"); g, beta and the state are fp32.  Both sides then consume
 exactly these rounded values (the oracle upcasts them to fp64).
 """
 from __future__ import annotations
@@ -47,7 +47,7 @@ class Workload:
     V: int
     chunk: int = 64
     per_channel: bool = False
-    dtype: str = "bf16"          # storage type of q, k, v: "fp32" or "bf16"
+    dtype: str = "bf16"          # storage type of q, k, v: "fp32", "bf16" or "fp16"
     g_mu: float = 3.0            # g = logsigmoid(N(g_mu, 1))
     s0_std: float = 0.0          # 0 -> no initial state
     seed: int = 42
@@ -156,6 +156,9 @@ def _store(x: np.ndarray, dtype: str):
     if dtype == "bf16":
         bits = bf16_round(x)
         return bf16_bits_to_f64(bits), bits
+    if dtype == "fp16":
+        h = np.ascontiguousarray(x, dtype=np.float16)    # round to nearest even
+        return h.astype(np.float64), h.view(np.uint16)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

@@ -42,11 +42,12 @@
  * is launched and a status other than GDR_OK is returned; no exception
  * crosses the ABI.  gdr_status_string() names every status.
  *
- * Numerics: with GDR_BF16 inputs the matrix products run on MFMA with fp16
- * operands and fp32 accumulation; the state, gamma, exponentials and o are
- * fp32 (o is rounded to bf16 only as it is stored, when o_dtype asks).
- * bf16 inputs must have |x| < 65504 (the fp16 range).  With GDR_F32
- * inputs every product runs in fp32.  With bf16 inputs the decay is folded
+ * Numerics: with GDR_BF16 or GDR_F16 inputs the matrix products run on
+ * MFMA with fp16 operands and fp32 accumulation (fp16 inputs are operands
+ * as they are); the state, gamma, exponentials and o are fp32 (o is rounded
+ * to bf16 or fp16 only as it is stored, when o_dtype asks).  bf16 inputs
+ * must have |x| < 65504 (the fp16 range).  With GDR_F32 inputs every
+ * product runs in fp32.  With 16-bit inputs the decay is folded
  * into fp16 operands, which grow as exp(sum of the positive g of a channel,
  * or of the row decay, within one chunk): that sum must stay at or below 8
  * (g <= 0, the usual log-decay, is always in range).  The state enters its
@@ -90,7 +91,7 @@ typedef enum gdr_status {
  * the process ends. */
 #define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
-typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1, GDR_F16 = 2 } gdr_dtype;
 
 /* The state update.  GDR_RULE_DELTA is the gated delta rule above.
  * GDR_RULE_LINEAR drops its prediction (erase) term,
@@ -129,14 +130,14 @@ typedef struct gdr_problem {
                                 they enter a product.  0: q and k are used as
                                 given */
   int32_t rule;              /* gdr_rule: GDR_RULE_DELTA (0) or GDR_RULE_LINEAR */
-  int32_t o_dtype;           /* gdr_dtype of o: GDR_F32 (0, the default) or
-                                GDR_BF16, the fp32 result rounded once to
-                                nearest even as it is stored (the scalar-g
-                                kernel page casts its output back to the
-                                input dtype).  Rounding o alone to bf16
-                                costs about 2e-2 relative to max|o| / rms(o)
-                                on the workloads, so fp32 is the form whose
-                                accuracy the library states. */
+  int32_t o_dtype;           /* gdr_dtype of o: GDR_F32 (0, the default),
+                                GDR_BF16 or GDR_F16, the fp32 result rounded
+                                once to nearest even as it is stored (the
+                                scalar-g kernel page casts its output back
+                                to the input dtype).  Rounding o alone to
+                                bf16 costs about 2e-2 relative to max|o| /
+                                rms(o) on the workloads, so fp32 is the form
+                                whose accuracy the library states. */
 } gdr_problem;
 
 /* Bytes of device workspace gdr_chunk_fwd needs for problem `p`, or 0 when
@@ -233,7 +234,7 @@ gdr_status gdr_chunk_scan(const gdr_problem* p,
  *   state_in  [B, HV, K, V] fp32, or NULL for a zero state
  *   state_out [B, HV, K, V] fp32 (required); state_out == state_in updates
  *             the state in place (a partial overlap is GDR_ERR_ALIAS)
- *   o     [B, HV, V] o_dtype (fp32 or bf16)
+ *   o     [B, HV, V] o_dtype (fp32, bf16 or fp16)
  * No workspace.  Validation, errors and streams as for gdr_chunk_fwd.  The
  * kernel reads and writes the state once: it is bound by HBM bandwidth. */
 gdr_status gdr_decode_step(const gdr_problem* p,
@@ -244,11 +245,12 @@ gdr_status gdr_decode_step(const gdr_problem* p,
 
 /* Bits of the word gdr_check_inputs writes. */
 typedef enum gdr_check_bit {
-  GDR_CHECK_NONFINITE = 1,   /* a NaN or an infinity in q, k, v, g or beta */
+  GDR_CHECK_NONFINITE = 1,   /* a NaN or an infinity in q, k, v, g or beta
+                                (in the encoding of their dtype) */
   GDR_CHECK_FP16_RANGE = 2,  /* bf16 q, k or v with |x| >= 65520, which rounds to
                                 infinity in fp16 (q and k are exempt with
                                 qk_l2norm = 1: they are scaled in fp32 first) */
-  GDR_CHECK_DECAY_RANGE = 4  /* bf16 inputs: within some chunk of the problem's
+  GDR_CHECK_DECAY_RANGE = 4  /* 16-bit inputs: within some chunk of the problem's
                                 chunk length, the positive g of one channel (or
                                 of the row decay) sum to more than 8 */
 } gdr_check_bit;

@@ -6,7 +6,7 @@ from __future__ import annotations
 import numpy as np
 
 # max|delta| / rms(ref) bounds for o and the final state
-TOL = {"fp32": 1e-3, "bf16": 2e-2}
+TOL = {"fp32": 1e-3, "bf16": 2e-2, "fp16": 2e-2}
 
 
 def rel_err(x, ref) -> float:
@@ -38,9 +38,11 @@ def to_device(inp, device="cuda"):
     """torch tensors on `device` holding exactly the generated values."""
     import torch
 
+    half = torch.float16 if inp.w.dtype == "fp16" else torch.bfloat16
+
     def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        if a.dtype == np.uint16:          # 16-bit storage: bf16 or fp16 bits
+            return torch.from_numpy(a.view(np.int16)).view(half).to(device)
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
     s0 = None if inp.s0 is None else dev(inp.s0)

@@ -15,7 +15,14 @@ gdr_status launch_scan128_f16(const Prob&, ScanArgs&, hipStream_t) { return GDR_
 gdr_status launch_scan128_f32(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan32_f16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
 gdr_status launch_scan32_f32(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
-gdr_status launch_decode(int, int, int, bool, bool, DecodeArgs&, hipStream_t) {
+gdr_status launch_prep_h16(const Prob&, PrepArgs&, bool, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_prep128_h16(const Prob&, PrepArgs&, bool, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_prep32_h16(const Prob&, PrepArgs&, bool, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_scan_h16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_scan_h16_linear(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_scan128_h16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_scan32_h16(const Prob&, ScanArgs&, hipStream_t) { return GDR_ERR_HIP; }
+gdr_status launch_decode(int, int, int, bool, int, DecodeArgs&, hipStream_t) {
   return GDR_ERR_HIP;
 }
 gdr_status launch_check(const Prob&, CheckArgs&, hipStream_t) { return GDR_ERR_HIP; }

@@ -319,21 +319,29 @@ def test_rule_validation(lib):
 
 
 def test_o_dtype_validation(lib):
-    """o_dtype must be a gdr_dtype; a bf16 o spans half the bytes of an fp32 one."""
+    """o_dtype and qkv_dtype must be gdr_dtypes (fp32, bf16, fp16); a 16-bit o
+    spans half the bytes of an fp32 one."""
     name = lambda st: binding.STATUS_NAMES[st]
     bad = base(T=100)
-    bad.o_dtype = 2
+    bad.o_dtype = 3
     assert name(call_fwd(lib, bad)) == "GDR_ERR_DTYPE"
     assert gdr.workspace_size(bad) == 0
+    bad.o_dtype = 2                     # fp16 o
+    assert gdr.workspace_size(bad) == gdr.workspace_size(base(T=100))
+    h16 = base(T=100, dtype="fp16")
+    assert gdr.workspace_size(h16) == gdr.workspace_size(base(T=100))
+    h16.qkv_dtype = 3
+    assert name(call_fwd(lib, h16)) == "GDR_ERR_DTYPE"
     bad1 = base(T=1)
     bad1.o_dtype = -1
     assert name(call_decode(lib, bad1)) == "GDR_ERR_DTYPE"
     # o placed just below v: B*T*HV*V = 51200 elements, 204800 bytes in fp32
     # (overlaps v) and 102400 in bf16 (does not)
-    p32, p16 = base(T=100), base(T=100, o_dtype="bf16")
+    p32, p16, ph = base(T=100), base(T=100, o_dtype="bf16"), base(T=100, o_dtype="fp16")
     o_at = 3 * A - 150000
     assert name(call_fwd(lib, p32, o=o_at)) == "GDR_ERR_ALIAS"
     assert name(call_fwd(lib, p16, o=o_at)) != "GDR_ERR_ALIAS"
+    assert name(call_fwd(lib, ph, o=o_at)) != "GDR_ERR_ALIAS"
     assert gdr.workspace_size(p16) == gdr.workspace_size(p32)
 
 
