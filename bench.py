@@ -216,9 +216,12 @@ def bench_decode(args, w, inp):
     import torch
     import chunkwise_gated_delta_cumsum_amd as gdr
 
+    from chunkwise_gated_delta_cumsum_amd.inputs import workload
+    half = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+
     def to_dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        if a.dtype == np.uint16:          # 16-bit storage: bf16 or fp16 bits
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(half).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     tok = dict(q=to_dev(inp.q_dev[:, 0]), k=to_dev(inp.k_dev[:, 0]), v=to_dev(inp.v_dev[:, 0]),
@@ -280,7 +283,9 @@ def bench_decode(args, w, inp):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(w, ("decode_step_kernel",), {
-                         **COUNTER_SETTING, "rule": args.rule, "slab": args.slab}),
+                         **COUNTER_SETTING, "rule": args.rule, "slab": args.slab,
+                         **({"dtype": w.dtype} if w.dtype != workload(args.workload).dtype
+                            else {})}),
                      "kernel": "decode_step", "kernels": ["decode_step_kernel"],
                      "algorithmic_bytes": nbytes, "kernel_ms": {"decode_step": kernel_ms}},
     }
@@ -325,6 +330,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, choices=(0, 32, 64, 128),
                     help="chunk length (0: the workload's, 64)")
+    ap.add_argument("--dtype", default="", choices=("", "bf16", "fp16", "fp32"),
+                    help="storage type of q, k, v (default: the workload's)")
     ap.add_argument("--segments", type=int, default=0,
                     help="sequence segments of the state scan (0: the library's choice)")
     ap.add_argument("--slab", type=int, default=0, choices=(0, 32, 64, 128),
@@ -357,8 +364,11 @@ def main():
 
     gdr.load()
     w = workload(args.workload)
+    own_dtype = w.dtype
     if args.chunk:
         w = w.with_(chunk=args.chunk)
+    if args.dtype:
+        w = w.with_(dtype=args.dtype)
     inp = make_inputs(w)
     if w.T == 1:
         bench_decode(args, w, inp)
@@ -469,6 +479,8 @@ def main():
     dom_bytes = tm["stage"][dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     setting = {"rule": args.rule, "chunk": w.chunk, "segments": args.segments, "slab": args.slab}
+    if w.dtype != own_dtype:   # the stored counters were taken in the workload's own dtype
+        setting["dtype"] = w.dtype
     traffic = measured_traffic(w, dom_kernels, setting)
     nseg = gdr.scan_segments(prob)
     slab = gdr.scan_slab(prob)
