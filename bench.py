@@ -332,6 +332,8 @@ def main():
                     help="chunk length (0: the workload's, 64)")
     ap.add_argument("--dtype", default="", choices=("", "bf16", "fp16", "fp32"),
                     help="storage type of q, k, v (default: the workload's)")
+    ap.add_argument("--seed", type=int, default=-1,
+                    help="seed of the synthetic inputs (default: the workload's)")
     ap.add_argument("--segments", type=int, default=0,
                     help="sequence segments of the state scan (0: the library's choice)")
     ap.add_argument("--slab", type=int, default=0, choices=(0, 32, 64, 128),
@@ -369,6 +371,8 @@ def main():
         w = w.with_(chunk=args.chunk)
     if args.dtype:
         w = w.with_(dtype=args.dtype)
+    if args.seed >= 0:
+        w = w.with_(seed=args.seed)
     inp = make_inputs(w)
     if w.T == 1:
         bench_decode(args, w, inp)

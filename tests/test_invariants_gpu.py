@@ -20,6 +20,10 @@ powers of two scale floating-point values exactly.
   largest value there (measured 1e-4; a missing or doubled scale is off by
   a factor of two).
 
+* A NaN stays in its scan: a NaN in the v of one (batch, value head) leaves
+  every other scan's o and final state bit-identical, and a NaN in the q/k
+  of one head reaches only the value heads of its group.
+
 Both decay forms, grouped heads, an initial state and a length that is not a
 multiple of the chunk are covered; the segmented scan is covered by the
 batch split at 3 forced segments.
@@ -98,3 +102,26 @@ def test_doubling_the_scale_doubles_o(gpu_lib, per_channel, dtype):
         assert np.array_equal(o2, 2.0 * o)
     else:
         assert dev <= 2e-3, dev
+
+
+@pytest.mark.parametrize("per_channel,segments", [(False, 1), (True, 1), (False, 3)],
+                         ids=["row", "pc", "row-seg3"])
+def test_nan_stays_in_its_scan(gpu_lib, per_channel, segments):
+    inp = make_inputs(small(per_channel, B=2, H=2, HV=4))
+    t = to_device(inp)
+    knobs = dict(segments=segments, slab=64)
+    o, s = fwd(gpu_lib, t, inp.scale, **knobs)
+    G = inp.w.G
+    for name, idx, hit in (("v", (1, 50, 2, 7), {(1, 2)}),
+                           ("k", (0, 130, 1, 3), {(0, hv) for hv in range(G, 2 * G)})):
+        tn = dict(t)
+        tn[name] = t[name].clone()
+        tn[name][idx] = float("nan")
+        on, sn = fwd(gpu_lib, tn, inp.scale, **knobs)
+        for b in range(inp.w.B):
+            for hv in range(inp.w.HV):
+                if (b, hv) in hit:
+                    assert not np.isfinite(sn[b, hv]).all(), (name, b, hv)
+                else:
+                    assert np.array_equal(on[b, :, hv], o[b, :, hv]), (name, b, hv)
+                    assert np.array_equal(sn[b, hv], s[b, hv]), (name, b, hv)
