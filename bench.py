@@ -159,20 +159,44 @@ def usable_cores():
     return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
 
 
-def cpu_baseline(inp, budget_s, rule="delta", single_thread=False):
+# Parity bound of the GPU result against the oracle, max |delta| / rms(ref)
+# (the 16-bit bound covers the fp16 MFMA operands; fp32 inputs keep fp32).
+PARITY_TOL = {"fp32": 1e-3, "bf16": 2e-2, "fp16": 2e-2}
+
+
+def _rel_err(x, ref):
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt((ref ** 2).mean()))
+    d = float(np.abs(x - ref).max()) if x.size else 0.0
+    return d / rms if rms > 0 else d
+
+
+def cpu_baseline(inp, budget_s, rule="delta", single_thread=False, gpu_out=None,
+                 gpu_what="o of a timed call"):
     """The fp64 oracle recurrence on the host cores, over a bounded sample of
     the workload: all (batch, value head) scans over a token prefix sized to
     about budget_s / 2 seconds per pass, repeated to about budget_s.  Reports
     the median pass as tokens/s, with the fastest pass, the thread count and
-    the CPU model; with single_thread, also one thread on a short prefix."""
+    the CPU model; with single_thread, also one thread on a short prefix.
+
+    gpu_out(Ts) -> (o [B, Ts, HV, V], final state or None) gives the GPU's
+    result (``gpu_what``) on the same prefix (o is causal, so the prefix of
+    the full sequence's o is the prefix's o; the final state only where the
+    prefix is the whole sequence): it is compared with the last pass's
+    result under ``parity``."""
     import oracle
     w = inp.w
     threads = min(usable_cores(), w.B * w.HV)
+    last = {}
 
     def run(Ts, nthreads):
         t0 = time.perf_counter()
-        oracle.recurrence(inp.q[:, :Ts], inp.k[:, :Ts], inp.v[:, :Ts], inp.g[:, :Ts],
-                          inp.beta[:, :Ts], inp.scale, inp.s0, threads=nthreads, rule=rule)
+        last["res"] = oracle.recurrence(inp.q[:, :Ts], inp.k[:, :Ts], inp.v[:, :Ts],
+                                        inp.g[:, :Ts], inp.beta[:, :Ts], inp.scale, inp.s0,
+                                        threads=nthreads, rule=rule)
+        last["T"] = Ts
         return time.perf_counter() - t0
 
     probe_T = min(w.T, 256)
@@ -190,6 +214,19 @@ def cpu_baseline(inp, budget_s, rule="delta", single_thread=False):
                       f"{w.B * w.HV} (batch, value head) scans, "
                       f"{'all' if Ts == w.T else 'first'} {Ts} of {w.T} tokens, "
                       f"{len(times)} passes, median {med:.2f} s, min {times[0]:.2f} s")}
+    if gpu_out is not None:
+        ro, rs = last["res"]
+        o_gpu, s_gpu = gpu_out(Ts)
+        tol = PARITY_TOL[w.dtype]
+        err_o = _rel_err(o_gpu, ro)
+        err_s = None if s_gpu is None else _rel_err(s_gpu, rs)
+        rec["parity"] = {
+            "what": ("max |GPU - oracle| / rms(oracle) over every (batch, value head) scan, "
+                     f"on {gpu_what}" + (" and its final state" if s_gpu is not None
+                                          else "") + f", first {Ts} of {w.T} tokens"),
+            "err_o": err_o, "err_state": err_s, "tol": tol,
+            "pass": bool(err_o <= tol and (err_s is None or err_s <= tol))}
+        last.clear()
     if single_thread:
         T1 = min(w.T, 256)
         t1 = sorted(run(T1, 1) for _ in range(3))[1]
@@ -290,7 +327,17 @@ def bench_decode(args, w, inp):
                      "algorithmic_bytes": nbytes, "kernel_ms": {"decode_step": kernel_ms}},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule)
+        # one more step in the timed configuration from the initial state
+        d = sets[0]
+        o1 = torch.empty_like(d["o"])
+        s1 = torch.empty_like(s0)
+        gdr.gdr_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s0, scale=inp.scale,
+                            out=(o1, s1), slab=args.slab, rule=args.rule)
+        torch.cuda.synchronize()
+        rec["cpu_baseline"] = cpu_baseline(
+            inp, args.cpu_budget, args.rule,
+            gpu_out=lambda Ts: (o1.cpu().numpy()[:, None], s1.cpu().numpy()),
+            gpu_what="o of one step in the timed configuration from the initial state")
     print(json.dumps(rec), flush=True)
 
 
@@ -541,8 +588,11 @@ def main():
                             step_each[len(step_each) // 2] * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.rule,
-                                           single_thread=w.name in SINGLE_THREAD_BASELINE)
+        d = sets[0]   # o and the final state of the path check above
+        rec["cpu_baseline"] = cpu_baseline(
+            inp, args.cpu_budget, args.rule, single_thread=w.name in SINGLE_THREAD_BASELINE,
+            gpu_out=lambda Ts: (d["o"][:, :Ts].cpu().numpy(),
+                                d["sT"].cpu().numpy() if Ts == w.T else None))
     print(json.dumps(rec), flush=True)
 
 
