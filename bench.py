@@ -136,6 +136,30 @@ def measured_mfma(w, setting=COUNTER_SETTING):
     return out or None
 
 
+class Ranges:
+    """roctx ranges (torch.cuda.nvtx is roctx on ROCm) around launches, when
+    enabled: ``with ranges(name):`` pushes the range before the launch and
+    pops it after.  Host-side marks only; used outside the timed steps."""
+
+    def __init__(self, enabled):
+        self.enabled = enabled
+
+    def __call__(self, name, active=True):
+        import contextlib
+        if not (self.enabled and active):
+            return contextlib.nullcontext()
+        import torch
+
+        @contextlib.contextmanager
+        def rng():
+            torch.cuda.nvtx.range_push(name)
+            try:
+                yield
+            finally:
+                torch.cuda.nvtx.range_pop()
+        return rng()
+
+
 # the small workloads whose oracle time is also reported on one thread
 SINGLE_THREAD_BASELINE = ("tiny_fp32_T256_H2_D64", "gdn_bf16_T4096_H12_D128")
 
@@ -290,9 +314,11 @@ def bench_decode(args, w, inp):
     # events on the launch stream
     KI = max(K, 20)
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ranges = Ranges(args.trace)
     a0.record()
     for i in range(KI):
-        step(sets[i % nsets])
+        with ranges("decode_step"):
+            step(sets[i % nsets])
     a1.record()
     torch.cuda.synchronize()
     kernel_ms = a0.elapsed_time(a1) / KI
@@ -370,6 +396,13 @@ def main():
     # 3% above the per-step event median; from 100 on the two agree
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=WORKLOAD_DEFAULT)
+    ap.add_argument("--config", type=int, default=-1,
+                    help="the workload by its index in the workload table (0-4: tiny fp32, "
+                         "4096 tokens, per channel, grouped heads, 65536 tokens); "
+                         "overrides --workload")
+    ap.add_argument("--trace", action="store_true",
+                    help="roctx ranges around each stage of the untimed per-stage run "
+                         "(chunk_prep, state_scan; decode_step), for rocprofv3 --marker-trace")
     ap.add_argument("--sets", type=int, default=0,
                     help="rotating input/output copies (0: enough to exceed 640 MiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -412,6 +445,8 @@ def main():
     from chunkwise_gated_delta_cumsum_amd.inputs import make_inputs, workload
 
     gdr.load()
+    if args.config >= 0:
+        args.workload = workload(args.config).name
     w = workload(args.workload)
     own_dtype = w.dtype
     if args.chunk:
@@ -454,15 +489,19 @@ def main():
         d["sT"] = torch.empty((w.B, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
         sets.append(d)
 
+    ranges = Ranges(args.trace)
+
     def step(d, e0=None, e1=None, e2=None):
         if e0 is not None:
             e0.record()
-        gdr.gdr_chunk_prep(d["q"], d["k"], d["g"], d["beta"], chunk=w.chunk, scale=inp.scale,
-                           V=w.V, workspace=d["ws"], **knobs)
+        with ranges("chunk_prep", e0 is not None):
+            gdr.gdr_chunk_prep(d["q"], d["k"], d["g"], d["beta"], chunk=w.chunk,
+                               scale=inp.scale, V=w.V, workspace=d["ws"], **knobs)
         if e1 is not None:
             e1.record()
-        gdr.gdr_chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["ws"], d["s0"],
-                           chunk=w.chunk, scale=inp.scale, out=(d["o"], d["sT"]), **knobs)
+        with ranges("state_scan", e0 is not None):
+            gdr.gdr_chunk_scan(d["q"], d["k"], d["v"], d["g"], d["beta"], d["ws"], d["s0"],
+                               chunk=w.chunk, scale=inp.scale, out=(d["o"], d["sT"]), **knobs)
         if e2 is not None:
             e2.record()
 
