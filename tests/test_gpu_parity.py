@@ -181,6 +181,18 @@ def test_positive_g(gpu_lib, per_channel, T, seed):
         check(o, s, ro, rs, "bf16", "positive g")
 
 
+@pytest.mark.parametrize("per_channel", [False, True], ids=["row", "pc"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_no_decay(gpu_lib, per_channel, dtype):
+    """g = 0 everywhere: DeltaNet without decay (the Chunkwise parallel
+    algorithms page, section 2.4, is this special case), through the decay
+    paths of both kernels, with an initial state and a ragged length."""
+    inp = make_inputs(small(per_channel=per_channel, dtype=dtype, T=300))
+    inp.g[...] = 0.0
+    o, s = run_gpu(gpu_lib, inp)
+    check(o, s, *oracle_full(inp), dtype, f"no decay pc={per_channel}")
+
+
 @pytest.mark.parametrize("mu", [-1.0, -3.0])
 def test_per_channel_strong_decay(gpu_lib, mu):
     """Per-channel g = logsigmoid(N(mu, 1)): decays of e^-1..e^-3 per token, so

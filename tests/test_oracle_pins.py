@@ -419,6 +419,43 @@ def test_linear_rule_page_form_and_delta_difference():
     np.testing.assert_array_equal(s1, s2)
 
 
+# ------------------------------------------- DeltaNet without decay -------
+def test_deltanet_without_decay_page_chunk_form():
+    """Chunkwise parallel algorithms page, section 2.4 (the matrix iteration
+    form of DeltaNet, no decay), with the UT transform of section 2.3: per
+    chunk, with T = (I + strictLower(diag(beta) K K^T))^-1 diag(beta),
+    W = T K and U = T V, and the state S' in the page's orientation (d_v x
+    d_k, the transpose of the oracle's),
+        O = Q S'^T + (Q K^T * M)(U - W S'^T),   S' <- S' + (U - W S'^T)^T K,
+    with M the causal mask.  The mask is read as including its diagonal (each
+    token's output sees its own write, as in the recurrence).  With g = 0 and
+    a unit scale the oracle's recurrence gives the same o and final state,
+    chunk after chunk; excluding the diagonal from M does not."""
+    rng = np.random.default_rng(24)
+    K, V, C, nch = 8, 6, 5, 3
+    T = C * nch
+    q, k, v, _, beta, S0 = rnd_problem(rng, B=1, T=T, H=1, HV=1, K=K, V=V, s0=True)
+    g = np.zeros((1, T, 1))
+    o, s = oracle.recurrence(q, k, v, g, beta, 1.0, S0)
+
+    def page_form(diag):
+        Sp = S0[0, 0].T.copy()
+        M = np.tril(np.ones((C, C)), 0 if diag else -1)
+        outs = []
+        for c in range(nch):
+            sl = slice(c * C, (c + 1) * C)
+            Qc, Kc, Vc, b = q[0, sl, 0], k[0, sl, 0], v[0, sl, 0], beta[0, sl, 0]
+            Tm = np.linalg.inv(np.eye(C) + np.tril(np.diag(b) @ Kc @ Kc.T, -1)) @ np.diag(b)
+            R = Tm @ Vc - (Tm @ Kc) @ Sp.T
+            outs.append(Qc @ Sp.T + (Qc @ Kc.T * M) @ R)
+            Sp = Sp + R.T @ Kc
+        return np.concatenate(outs)[None, :, None], Sp.T[None, None]
+
+    po, ps = page_form(True)
+    assert rel(po, o) < 1e-12 and rel(ps, s) < 1e-12
+    assert rel(page_form(False)[0], o) > 1e-2
+
+
 # ------------------------------------------------- per-head recurrence ------
 @pytest.mark.parametrize("per_channel", [False, True])
 def test_recurrence_heads_equals_full_recurrence(per_channel):
