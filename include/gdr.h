@@ -17,13 +17,13 @@
  * floating-point rounding.
  *
  * Tensor layouts (row-major, contiguous, device memory):
- *   q, k           [B, T, H, K]    qkv_dtype (GDR_F32 or GDR_BF16)
+ *   q, k           [B, T, H, K]    qkv_dtype (GDR_F32, GDR_BF16 or GDR_F16)
  *   v              [B, T, HV, V]   qkv_dtype
  *   g              [B, T, HV] fp32 (one log-decay per value head), or
  *                  [B, T, HV, K] fp32 when g_per_channel = 1 (KDA form)
  *   beta           [B, T, HV]      fp32
  *   initial_state  [B, HV, K, V]   fp32, or NULL for a zero state
- *   o              [B, T, HV, V]   o_dtype: fp32, or bf16 (output)
+ *   o              [B, T, HV, V]   o_dtype: fp32, bf16 or fp16 (output)
  *   final_state    [B, HV, K, V]   fp32 (output), or NULL to skip
  *
  * Ownership: the caller allocates and owns every buffer, the workspace
