@@ -193,6 +193,20 @@ def test_no_decay(gpu_lib, per_channel, dtype):
     check(o, s, *oracle_full(inp), dtype, f"no decay pc={per_channel}")
 
 
+@pytest.mark.parametrize("per_channel", [False, True], ids=["row", "pc"])
+@pytest.mark.parametrize("T", [64, 100])
+def test_many_short_sequences(gpu_lib, per_channel, T):
+    """A wide batch of short sequences (48 x 4 value heads = 192 scans of one
+    or two chunks, grouped heads, an initial state): many workgroups per
+    launch, each with a short chunk loop, and the automatic scan choice for
+    many scans, against the whole oracle."""
+    w = Workload("wide", B=48, T=T, H=2, HV=4, K=128, V=128, per_channel=per_channel,
+                 dtype="bf16", g_mu=4.0 if per_channel else 3.0, s0_std=0.1, seed=91)
+    inp = make_inputs(w)
+    o, s = run_gpu(gpu_lib, inp)
+    check(o, s, *oracle_full(inp), "bf16", f"48 sequences of {T} pc={per_channel}")
+
+
 @pytest.mark.parametrize("mu", [-1.0, -3.0])
 def test_per_channel_strong_decay(gpu_lib, mu):
     """Per-channel g = logsigmoid(N(mu, 1)): decays of e^-1..e^-3 per token, so
