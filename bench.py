@@ -220,7 +220,6 @@ def cpu_baseline(inp, budget_s, rule="delta", single_thread=False, gpu_out=None,
         last["res"] = oracle.recurrence(inp.q[:, :Ts], inp.k[:, :Ts], inp.v[:, :Ts],
                                         inp.g[:, :Ts], inp.beta[:, :Ts], inp.scale, inp.s0,
                                         threads=nthreads, rule=rule)
-        last["T"] = Ts
         return time.perf_counter() - t0
 
     probe_T = min(w.T, 256)
