@@ -267,6 +267,46 @@ __device__ __forceinline__ void fold_aqk(const f32x4 (&aqT)[C / 16], const float
   }
 }
 
+// ---- the linear rule (M = I): W^ = diag(s) k and A^ = A_qk, no products ------
+// fold_w and fold_aqk with M^-T = I, element by element: the same accumulator
+// tiles (lane: column r, rows 4 grp + j) and the same stores.  Each W^ entry
+// is rounded once from fp32 (the product path rounds s to fp16 first); A^
+// equals the product path's bits (I times an fp16 value is exact).
+template <int K, int C, class P, bool kRowScale, class KVal, class RScale>
+__device__ __forceinline__ void fold_w_identity(typename P::ws_t* wt_chunk, int wave, int lane,
+                                                int r, int grp, KVal kval, RScale rscale) {
+  constexpr int NB = C / 16, CB = C / 32;
+  using ws_t = typename P::ws_t;
+  for (int jd = wave; jd < K / 16; jd += NB) {
+    const int d = chan_of_row(16 * jd + r);
+    f32x4 acc[NB];
+#pragma unroll
+    for (int Ic = 0; Ic < NB; ++Ic)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 16 * Ic + 4 * grp + j;
+        acc[Ic][j] = kRowScale ? kval(c, d) * rscale(c) : kval(c, d);
+      }
+    ws_t* wt = wt_chunk + (size_t)jd * CB * 512;
+#pragma unroll
+    for (int kb = 0; kb < CB; ++kb)
+      store_ws(wt + kb * 512 + lane * 8, acc[2 * kb], acc[2 * kb + 1]);
+  }
+}
+
+template <int C, class P>
+__device__ __forceinline__ void fold_aqk_identity(const f32x4 (&aqT)[C / 16],
+                                                  typename P::ws_t* ah_chunk, int wave,
+                                                  int lane) {
+  constexpr int CB = C / 32;
+  const int Ii = wave;
+#pragma unroll
+  for (int kb = 0; kb < CB; ++kb) {
+    if (kb > Ii / 2) continue;
+    store_ws(ah_chunk + (size_t)ah_frag(Ii, kb) * 512 + lane * 8, aqT[2 * kb], aqT[2 * kb + 1]);
+  }
+}
+
 // ---- inspection dumps shared by both kernels ---------------------------------
 template <int C>
 __device__ __forceinline__ void dump_akk(float* out, const float* sL, int tid) {
@@ -590,10 +630,13 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kernel(PrepArgs a) {
   }
 
   // ---- 3. M^-1 (M^-T replaces A_kk in sL) ------------------------------------
-  if (a.linear)
-    identity_inverse<C>(sL, tid);
-  else
+  // (the linear rule has M = I: nothing to invert; the identity is written
+  // only for the inspection dump)
+  if (a.linear) {
+    if constexpr (DUMP) identity_inverse<C>(sL, tid);
+  } else {
     unit_lower_inverse<C, P>(sL, wave, r, grp);
+  }
   GDR_PPROF(4);
 
   if constexpr (DUMP) {
@@ -601,14 +644,21 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kernel(PrepArgs a) {
   }
 
   // ---- 4a. W^ (beta exp(gamma_last - gamma) scales the rows of M^-T) -------
-  fold_w<K, C, P, true>(sL, static_cast<ws_t*>(a.wt) + (size_t)cid * K * C, wave, lane, r, grp,
-                        [&](int c, int d) { return P::in_to_f32(sK[c * KP + d]); },
-                        [&](int c) { return sKs[c] * sRk[c]; });
+  ws_t* const wt_chunk = static_cast<ws_t*>(a.wt) + (size_t)cid * K * C;
+  auto k_at = [&](int c, int d) { return P::in_to_f32(sK[c * KP + d]); };
+  auto w_scale = [&](int c) { return sKs[c] * sRk[c]; };
+  if (a.linear)
+    fold_w_identity<K, C, P, true>(wt_chunk, wave, lane, r, grp, k_at, w_scale);
+  else
+    fold_w<K, C, P, true>(sL, wt_chunk, wave, lane, r, grp, k_at, w_scale);
   GDR_PPROF(5);
 
   // ---- 4b. A^ ----------------------------------------------------------------
-  fold_aqk<C, P>(aqT, sL, static_cast<ws_t*>(a.ah) + (size_t)cid * ah_frags(C) * 512, wave, lane,
-                 r, grp);
+  ws_t* const ah_chunk = static_cast<ws_t*>(a.ah) + (size_t)cid * ah_frags(C) * 512;
+  if (a.linear)
+    fold_aqk_identity<C, P>(aqT, ah_chunk, wave, lane);
+  else
+    fold_aqk<C, P>(aqT, sL, ah_chunk, wave, lane, r, grp);
   GDR_PPROF(6);
 
   // ---- row scalars --------------------------------------------------------

@@ -490,20 +490,30 @@ __global__ __launch_bounds__(C * 4) void chunk_prep_kda_kernel(PrepArgs a) {
   }
 
   // ---- M^-1 (M^-T replaces A_kk in sL), then the folded operands -------------
-  if (a.linear)
-    identity_inverse<C>(sL, tid);
-  else
+  // (the linear rule: M = I, the identity written only for the dump, and the
+  // folds element by element)
+  if (a.linear) {
+    if constexpr (DUMP) identity_inverse<C>(sL, tid);
+  } else {
     unit_lower_inverse<C, P>(sL, wave, r, grp);
+  }
   GDR_PPROF(4);
   if constexpr (DUMP) {
     if (a.d_minv) dump_minv<C>(a.d_minv + (size_t)cid * C * C, sL, tid);
   }
-  fold_w<K, C, P, false>(sL, static_cast<ws_t*>(a.wt) + (size_t)cid * K * C, wave, lane, r, grp,
-                         [&](int c, int d) { return (float)sSK[c * SP + d]; },
-                         [&](int) { return 1.f; });
+  ws_t* const wt_chunk = static_cast<ws_t*>(a.wt) + (size_t)cid * K * C;
+  auto sk_at = [&](int c, int d) { return (float)sSK[c * SP + d]; };
+  auto unit = [&](int) { return 1.f; };
+  if (a.linear)
+    fold_w_identity<K, C, P, false>(wt_chunk, wave, lane, r, grp, sk_at, unit);
+  else
+    fold_w<K, C, P, false>(sL, wt_chunk, wave, lane, r, grp, sk_at, unit);
   GDR_PPROF(5);
-  fold_aqk<C, P>(aqT, sL, static_cast<ws_t*>(a.ah) + (size_t)cid * ah_frags(C) * 512, wave,
-                 lane, r, grp);
+  ws_t* const ah_chunk = static_cast<ws_t*>(a.ah) + (size_t)cid * ah_frags(C) * 512;
+  if (a.linear)
+    fold_aqk_identity<C, P>(aqT, ah_chunk, wave, lane);
+  else
+    fold_aqk<C, P>(aqT, sL, ah_chunk, wave, lane, r, grp);
   GDR_PPROF(6);
   GDR_PPROF_FLUSH;
 }
