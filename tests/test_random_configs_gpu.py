@@ -1,15 +1,15 @@
 """Parity on seeded random configurations across the supported space.
 
 The hand-written cases cover each option on its own and in the pairs the
-workloads use; this module draws 48 configurations at random from every
+workloads use; this module draws 72 configurations at random from every
 combination the C ABI accepts: chunk length (32, 64, 128), K and V (64,
 128), grouped heads (G = 1, 2, 4), one decay per value head or per key
-channel with slow or fast decays, bf16 or fp32 inputs, the delta or the
-linear rule, in-kernel q/k normalisation, forced scan segments and slab
-widths, an initial state, and ragged lengths (any T up to 5 chunks past a
-multiple).  Each runs gdr_chunk_fwd against the fp64 oracle recurrence with
-the bounds of the other parity tests (1e-3 for fp32 inputs, 2e-2 for bf16,
-on o and the final state).  The draws are seeded, so every run checks the
+channel with slow or fast decays, bf16 or fp32 inputs (draws 48-71 may
+also take fp16), the delta or the linear rule, in-kernel q/k normalisation,
+forced scan segments and slab widths, an initial state, and ragged lengths
+(any T up to 5 chunks past a multiple).  Each runs gdr_chunk_fwd against the
+fp64 oracle recurrence with the bounds of the other parity tests (1e-3 for
+fp32 inputs, 2e-2 for bf16 and fp16, on o and the final state).  The draws are seeded, so every run checks the
 same configurations; their parameters are printed with the errors.
 """
 import numpy as np
@@ -21,7 +21,8 @@ from helpers import TOL, rel_err, run_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CONFIGS = 48
+N_CONFIGS = 72
+N_BEFORE_FP16 = 48
 
 
 def draw(i):
@@ -35,6 +36,8 @@ def draw(i):
     T = int(rng.integers(1, 5 * C + 40))
     per_channel = bool(rng.random() < 0.4)
     dtype = "fp32" if rng.random() < 0.25 else "bf16"
+    if i >= N_BEFORE_FP16 and dtype == "bf16" and rng.random() < 0.6:
+        dtype = "fp16"
     rule = "linear" if rng.random() < 0.25 else "delta"
     l2norm = bool(rng.random() < 0.25)
     mu = float(rng.choice([1.0, 3.0, 5.0]))
