@@ -97,7 +97,12 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
   // token while the scan's serial steps only halve) and than 32-row ones
   // (twice the serial steps), so it is 64.
   r.C = p->chunk == 0 ? 64 : p->chunk;
-  r.N = (p->T + r.C - 1) / r.C;
+  r.N = (int)(((int64_t)p->T + r.C - 1) / r.C);   // T + C - 1 may pass INT_MAX
+  // grid sizes must fit a 32-bit launch dimension: B HV N workgroups and
+  // more; B HV is bounded first, so that no product here can wrap
+  const uint64_t bhv = (uint64_t)p->B * (uint64_t)p->HV;   // < 2^62
+  if (bhv > 0x7fffffffull || bhv * (uint64_t)r.N + 8ull * (uint64_t)p->HV > 0x7fffffffull)
+    return GDR_ERR_SHAPE;
   r.perch = p->g_per_channel == 1;
   r.f32 = p->qkv_dtype == GDR_F32;
   r.h16 = p->qkv_dtype == GDR_F16;
@@ -144,8 +149,6 @@ gdr_status validate(const gdr_problem* p, Prob* out) {
                      scan_cost(BH, r.K, r.V, 64, r.nseg, r.seg_len) * 0.85)
       r.bv = 32;
   }
-  // grid sizes must fit a 32-bit launch dimension
-  if ((uint64_t)r.B * r.HV * r.N + 8ull * r.HV > 0x7fffffffull) return GDR_ERR_SHAPE;
   if (out) *out = r;
   return GDR_OK;
 }

@@ -471,3 +471,82 @@ def test_chunk_length_problems(lib):
     nc = 12 * 64                       # value-head chunks of 64 rows
     assert w128 - w64 == (nc // 2) * (20 - 2 * 6) * 512 * 2 - (nc // 2) * 256 * 4
     assert gdr.scan_segments(base(T=4096, H=12, HV=12, chunk=128, segments=3)) == 3
+
+
+def test_grid_limit_cannot_wrap(lib):
+    """Shapes whose workgroup count B HV N passes 2^31 are GDR_ERR_SHAPE, also
+    where the 64-bit product B HV N would wrap to a small value (B = HV = 2^19
+    with N = 2^26 chunks of 32 rows is exactly 2^64) and where T + C - 1 passes
+    INT_MAX; the largest single sequence stays valid."""
+    M = 2 ** 31 - 1
+    wrap = gdr.problem(2 ** 19, M, 2 ** 19, 2 ** 19, 128, 128, chunk=32)
+    assert gdr.workspace_size(wrap) == 0
+    assert lib.gdr_chunk_scan_segments(ctypes.byref(wrap)) == 0
+    assert call_fwd(lib, wrap) == 2
+    assert gdr.workspace_size(gdr.problem(2 ** 16, 64, 1, 2 ** 16, 128, 128)) == 0
+    assert gdr.workspace_size(gdr.problem(M, M, M, M, 128, 128)) == 0
+    for chunk in (0, 32, 64, 128):
+        one = gdr.problem(1, M, 1, 1, 128, 128, chunk=chunk)
+        C = chunk or 64
+        assert gdr.workspace_size(one) >= -(-M // C) * 128 * C * 2   # W^ alone
+        assert 1 <= lib.gdr_chunk_scan_segments(ctypes.byref(one)) <= -(-M // C)
+
+
+def _valid_by_the_header(B, T, H, HV, K, V, chunk, pc, scale, dtype, seg, slab, l2, rule, odt):
+    """The validity rules gdr.h states for gdr_problem, written out."""
+    import math
+    if min(B, T, H, HV, K, V) < 1 or HV % H:
+        return False
+    if dtype not in (0, 1, 2) or odt not in (0, 1, 2):
+        return False
+    if pc not in (0, 1) or l2 not in (0, 1) or rule not in (0, 1) or not math.isfinite(scale):
+        return False
+    if chunk not in (0, 32, 64, 128) or K not in (64, 128) or V not in (64, 128):
+        return False
+    if seg < 0 or slab not in (0, 32, 64):
+        return False
+    C = chunk or 64
+    if C == 128 and slab not in (0, 32 if K == 128 else 64):
+        return False
+    N = -(-T // C)
+    return B * HV * N + 8 * HV <= 2 ** 31 - 1
+
+
+def test_validation_fuzz(lib):
+    """Arbitrary field values, extreme ones included: the size, segment and
+    slab queries agree with each other and with the header's validity rules,
+    no call crashes, and a call with NULL buffers never reports success."""
+    from hypothesis import given, settings, strategies as st, HealthCheck
+    edge = st.sampled_from([-2 ** 31, -1, 0, 1, 2, 3, 32, 63, 64, 65, 127, 128, 2 ** 16,
+                            2 ** 19, 2 ** 24, 2 ** 31 - 1])
+    small = st.one_of(st.integers(-2, 300), edge)
+    field = st.one_of(st.integers(-2, 3), edge)
+    kv = st.one_of(st.sampled_from([64, 128]), small)
+
+    @settings(max_examples=600, deadline=None, derandomize=True,
+              suppress_health_check=list(HealthCheck))
+    @given(B=small, T=small, H=small, HV=small, K=kv, V=kv,
+           chunk=st.one_of(st.sampled_from([0, 32, 64, 128]), small), pc=field,
+           scale=st.floats(width=32), dtype=field, seg=small,
+           slab=st.one_of(st.sampled_from([0, 32, 64]), small), l2=field, rule=field,
+           odt=field)
+    def run(B, T, H, HV, K, V, chunk, pc, scale, dtype, seg, slab, l2, rule, odt):
+        p = binding.GdrProblem(B, T, H, HV, K, V, chunk, pc, scale, dtype, seg, slab, l2, rule,
+                               odt)
+        ws = lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p))
+        nseg = lib.gdr_chunk_scan_segments(ctypes.byref(p))
+        width = lib.gdr_chunk_scan_slab(ctypes.byref(p))
+        valid = _valid_by_the_header(B, T, H, HV, K, V, chunk, pc, scale, dtype, seg, slab, l2,
+                                     rule, odt)
+        assert (ws > 0) == valid and (nseg > 0) == valid and (width > 0) == valid
+        if valid:
+            N = -(-T // (chunk or 64))
+            assert 1 <= nseg <= N and width in (32, 64)
+            assert ws >= B * HV * N * K * (chunk or 64) * 2   # W^ alone
+        st_fwd = lib.gdr_chunk_fwd(ctypes.byref(p), *([None] * 8), None, 0, None)
+        st_dec = lib.gdr_decode_step(ctypes.byref(p), *([None] * 8), None)
+        st_chk = lib.gdr_check_inputs(ctypes.byref(p), *([None] * 6), None)
+        for s in (st_fwd, st_dec, st_chk):
+            assert s != 0 and lib.gdr_status_string(s)
+
+    run()
