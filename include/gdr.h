@@ -81,7 +81,9 @@ typedef enum gdr_status {
                               scan_segments < 0, or scan_slab not 0, 32 or 64
                               (gdr_decode_step also takes 128) */
   GDR_ERR_ALIAS = 10,      /* an output overlaps an input or the other output
-                              (final_state == initial_state exactly is allowed) */
+                              (final_state == initial_state exactly is allowed),
+                              or the workspace overlaps an input, a state or o;
+                              inputs may overlap each other (they are only read) */
   GDR_ERR_SCRATCH = 11     /* gdr_chunk_fwd_noalloc: the problem needs more
                               workspace than GDR_NOALLOC_SCRATCH_BYTES */
 } gdr_status;
