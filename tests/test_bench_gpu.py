@@ -39,6 +39,21 @@ def test_bench_line_tiny_fp32():
     assert par["pass"] and par["err_o"] <= 1e-3 and par["err_state"] <= 1e-3
 
 
+@pytest.mark.parametrize("flags,tol", [(("--rule", "linear"), 1e-3), (("--chunk", "128"), 1e-3),
+                                       (("--chunk", "32"), 1e-3), (("--dtype", "fp16"), 2e-2),
+                                       (("--config", "1", "--dtype", "fp16"), 2e-2)],
+                         ids=["linear", "c128", "c32", "fp16", "4096-fp16"])
+def test_bench_line_options(flags, tol):
+    """The launch-path options of the bench, each checked against the oracle
+    in the same run (the 4096-token workload's prefix sample for the last)."""
+    args = ("--config", "0") if "--config" not in flags else ()
+    rec = run_bench(*args, *flags, "--steps", "3", "--warmup", "2", "--cpu-budget", "0.5")
+    par = rec["cpu_baseline"]["parity"]
+    print(flags, rec["config"]["workload"], par, flush=True)
+    assert rec["fwd_entry_point_matches"] and par["pass"] and par["tol"] == tol
+    assert par["err_o"] <= tol and (par["err_state"] is None or par["err_state"] <= tol)
+
+
 def test_bench_line_decode():
     rec = run_bench("--workload", "decode_kda_bf16_B32_H16_D128", "--steps", "3", "--warmup", "2",
                     "--cpu-budget", "0.5")
