@@ -1,8 +1,8 @@
 """gdr_chunk_fwd_noalloc (the entry point without a workspace argument, on
 the library's own device scratch array) against gdr_chunk_fwd, through the
-C ABI: two calls in a row on one GPU, the second with a smaller problem, each
-equal to gdr_chunk_fwd bit for bit and to the fp64 oracle within the bounds
-of the parity tests."""
+C ABI: calls in a row on one GPU (the second with a smaller problem, the
+third with per-channel decay and fp16 inputs), each equal to gdr_chunk_fwd
+bit for bit and to the fp64 oracle within the bounds of the parity tests."""
 import numpy as np
 import pytest
 
@@ -32,6 +32,8 @@ def test_noalloc_two_calls_match_chunk_fwd(gpu_lib):
         (WORKLOADS[1], {}),
         # then a smaller one with grouped heads, an initial state and 3 segments
         (WORKLOADS[3].with_(B=1, T=700), dict(segments=3)),
+        # and a third on the same array: per-channel decay, fp16 inputs, 2 segments
+        (WORKLOADS[2].with_(B=1, T=300, dtype="fp16"), dict(segments=2)),
     ]
     for w, kw in cases:
         inp = make_inputs(w)
