@@ -60,3 +60,48 @@ def test_noalloc_refuses_large_problem(gpu_lib):
                                       t["initial_state"], scale=inp.scale)
     assert e.value.name == "GDR_ERR_SCRATCH"
     torch.cuda.synchronize()
+
+
+def test_noalloc_under_graph_capture(gpu_lib):
+    """The callers the entry point is for: captured into a HIP graph with
+    caller-owned outputs (nothing is allocated during the capture), replayed
+    with new contents in the captured input buffers and eager work in
+    between, each replay equal to gdr_chunk_fwd bit for bit."""
+    import torch
+    w = WORKLOADS[3].with_(B=1, T=700)
+    static = to_device(make_inputs(w))
+    o = torch.empty((w.B, w.T, w.HV, w.V), dtype=torch.float32, device="cuda")
+    s = torch.empty((w.B, w.HV, w.K, w.V), dtype=torch.float32, device="cuda")
+    scale = w.K ** -0.5
+
+    def args():
+        return (static["q"], static["k"], static["v"], static["g"], static["beta"],
+                static["initial_state"])
+
+    def call():
+        gpu_lib.gdr_chunk_fwd_noalloc(*args(), scale=scale, out=(o, s), segments=3)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up outside the capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        fresh = to_device(make_inputs(w.with_(seed=w.seed + 200 + rep)))
+        for name, x in fresh.items():
+            if x is not None:
+                static[name].copy_(x)
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        oe, se = gpu_lib.gdr_chunk_fwd(*args(), scale=scale, segments=3)
+        torch.cuda.synchronize()
+        print(f"noalloc graph replay {rep}: equal {torch.equal(o, oe) and torch.equal(s, se)}",
+              flush=True)
+        assert torch.equal(o, oe) and torch.equal(s, se), rep
